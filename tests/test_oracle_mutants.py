@@ -1,0 +1,101 @@
+"""One-line mutants of the oracle: each planted mistake must break at least one pin.
+
+The mutants are made on the CPU from the oracle's own source text (a single
+substring replaced), so they are plausible slips in the code as written: a
+dropped term, a wrong sign or bound, a swapped operand. The tiled-model
+mutants follow the spirit of the "five one-line bugs in an online-softmax
+kernel" exercise (Paper: FlashAttention, Exercises): no rescale of l, no
+rescale of the accumulator, an off-by-one causal mask, no -inf guard,
+normalising inside the loop, and more.
+"""
+
+import inspect
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.naive
+import oracle.tiled
+from oracle_pins import _close, failing_pins
+
+
+def _mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType(module.__name__ + "_mutant")
+    exec(compile(src.replace(old, new), module.__file__ + ":mutant", "exec"), mod.__dict__)
+    return mod
+
+
+NAIVE_MUTANTS = {
+    "causal-drops-diagonal": ("counts = np.minimum(counts, positions + 1)", "counts = np.minimum(counts, positions)"),
+    "padding-ignored": ("min(int(kv_len_b), int(n_keys))", "max(int(kv_len_b), int(n_keys))"),
+    "scale-dropped": ("s = scale * (q @ k[:kmax].T)", "s = (q @ k[:kmax].T)"),
+    "scale-squared": ("s = scale * (q @ k[:kmax].T)", "s = scale * scale * (q @ k[:kmax].T)"),
+    "no-max-subtraction": ("m = np.where(has, m, 0.0)", "m = np.where(has, 0.0, 0.0)"),
+    "max-over-masked-keys": ("m = np.max(s, axis=1, where=valid, initial=-np.inf)",
+                             "m = np.max(s, axis=1, initial=-np.inf)"),
+    "masked-keys-weighted": ("w = np.exp(np.where(valid, s - m[:, None], 0.0)) * valid",
+                             "w = np.exp(np.where(valid, s - m[:, None], 0.0))"),
+    "mask-off-by-one": ("valid = np.arange(kmax)[None, :] < counts[:, None]",
+                        "valid = np.arange(kmax)[None, :] <= counts[:, None]"),
+    "no-normalisation": ("o[has] = (w[has] @ v[:kmax]) / l[has, None]", "o[has] = (w[has] @ v[:kmax])"),
+    "keys-for-values": ("o[has] = (w[has] @ v[:kmax]) / l[has, None]", "o[has] = (w[has] @ k[:kmax]) / l[has, None]"),
+    "lse-drops-max": ("lse[has] = m[has] + np.log(l[has])", "lse[has] = np.log(l[has])"),
+    "lse-sign": ("lse[has] = m[has] + np.log(l[has])", "lse[has] = m[has] - np.log(l[has])"),
+    "empty-row-lse-zero": ("lse = np.full(n_rows, -np.inf)", "lse = np.full(n_rows, 0.0)"),
+    "softmax-wrong-axis": ("l = w.sum(axis=1)", "l = w.sum(axis=0)[:n_rows] if w.shape[1] >= n_rows else w.sum(axis=1)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NAIVE_MUTANTS))
+def test_naive_mutant_is_caught(name):
+    mod = _mutant(oracle.naive, *NAIVE_MUTANTS[name])
+    assert failing_pins(mod.attention), f"mutant {name} passes every pin"
+
+
+def test_unmutated_naive_passes_every_pin():
+    assert failing_pins(oracle.attention) == []
+
+
+TILED_MUTANTS = {
+    "no-rescale-l": ("l = correction * l + p.sum(axis=-1)", "l = l + p.sum(axis=-1)"),
+    "no-rescale-acc": ("acc = correction[..., None] * acc + np.matmul(p, v[:, :, k0:k1])",
+                       "acc = acc + np.matmul(p, v[:, :, k0:k1])"),
+    "causal-mask-ge": ("(cols[None, :] > rows[:, None])", "(cols[None, :] >= rows[:, None])"),
+    "no-inf-guard": ("m_sub = np.where(live, m_new, 0.0)", "m_sub = m_new"),
+    "normalise-in-loop": ("            m = m_new\n",
+                          "            m = m_new; acc = acc / np.where(l > 0, l, 1.0)[..., None]\n"),
+    "skip-diagonal-block": ("if causal and k0 > q1 - 1:", "if causal and k0 >= q1 - 1:"),
+    "correction-sign": ("np.exp(m - m_sub)", "np.exp(m_sub - m)"),
+    "stale-max": ("            m = m_new\n", "            pass\n"),
+}
+
+
+def _tiled_vs_naive(tiled):
+    """The check a tiled model must pass: naive results at several block sizes, with masked rows."""
+    rng = np.random.default_rng(31)
+    q = 2.0 * rng.standard_normal((2, 2, 23, 8))
+    k = rng.standard_normal((2, 2, 23, 8))
+    v = rng.standard_normal((2, 2, 23, 8))
+    kv = np.array([0, 19])
+    for causal in (False, True):
+        want = oracle.attention(q, k, v, 0.35, causal=causal, kv_len=kv)
+        for bq, bk in ((3, 5), (8, 8), (16, 7), (23, 2)):
+            with np.errstate(all="ignore"):
+                got = tiled(q, k, v, 0.35, causal=causal, kv_len=kv, block_q=bq, block_kv=bk)
+            _close(got[0], want[0], 1e-12, 1e-12, f"O causal={causal} bq={bq} bk={bk}")
+            _close(got[1], want[1], 1e-12, 1e-12, f"LSE causal={causal} bq={bq} bk={bk}")
+
+
+@pytest.mark.parametrize("name", sorted(TILED_MUTANTS))
+def test_tiled_mutant_is_caught(name):
+    mod = _mutant(oracle.tiled, *TILED_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        _tiled_vs_naive(mod.tiled_attention)
+
+
+def test_unmutated_tiled_passes():
+    _tiled_vs_naive(oracle.tiled_attention)
