@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput on one MI355X, as one JSON line on stdout.
+
+A step is one call of the HIP attention forward over the whole workload (one
+launch of the fused kernel: Q.K^T, masks, online softmax, P.V, normalisation and
+LSE). Inputs and outputs are resident in device memory before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+FLOPs are algorithmic: 4*D per unmasked (query, key) pair, so the causal
+triangle and padded keys are counted once and only where they are computed by
+the definition. The roofline figure divides those FLOPs by the kernel's own
+average duration, measured with events recorded on the launch stream around
+every timed launch.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s and % bf16 MFMA peak, B2 H32 N8192 D128 bf16"
+# MI355X published dense matrix peaks, TFLOP/s, and HBM3E bandwidth, GB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_tiled_attention_23_amd/csrc/fa_fwd_kernel.h", "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def pair_count(w, kv_len):
+    """Unmasked (query, key) pairs of the whole workload."""
+    import numpy as np
+    total = 0
+    i = np.arange(w.N, dtype=np.int64)
+    for b in range(w.B):
+        L = w.N if kv_len is None else int(kv_len[b])
+        cnt = np.minimum(L, i + 1) if w.causal else np.full(w.N, L, dtype=np.int64)
+        total += int(cnt.sum()) * w.H
+    return total
+
+
+def algorithmic_bytes(w, kv_len, elt):
+    """Q and O once, K and V rows that some query may see once, LSE once."""
+    rows_kv = w.B * w.N if kv_len is None else int(sum(int(x) for x in kv_len))
+    return elt * w.D * (2 * w.B * w.N + 2 * rows_kv) * w.H + 4 * w.B * w.H * w.N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it is still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, heads):
+    """The float64 oracle on the first `heads` (batch, head) pairs of the same inputs, all rows."""
+    import numpy as np
+    import oracle
+    from exact_tiled_attention_23_amd.workloads import to_f64
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads = min(heads, w.B * w.H)
+    sel = [divmod(i, w.H) for i in range(heads)]
+    q = np.stack([to_f64(x.q[b, h]) for b, h in sel])[None]
+    k = np.stack([to_f64(x.k[b, h]) for b, h in sel])[None]
+    v = np.stack([to_f64(x.v[b, h]) for b, h in sel])[None]
+    pairs = 0
+    i = np.arange(w.N, dtype=np.int64)
+    for b, _ in sel:
+        L = w.N if x.kv_len is None else int(x.kv_len[b])
+        pairs += int((np.minimum(L, i + 1) if w.causal else np.full(w.N, L)).sum())
+    t0 = time.perf_counter()
+    if x.kv_len is None:
+        oracle.attention(q, k, v, x.scale, causal=w.causal, workers=cores)
+    else:
+        # one (b, h) per call so each keeps its batch's kv_len
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        def one(j):
+            b = sel[j][0]
+            oracle.attention(q[:, j:j + 1], k[:, j:j + 1], v[:, j:j + 1], x.scale, causal=w.causal,
+                             kv_len=x.kv_len[b:b + 1])
+        with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=cores) as ex:
+            list(ex.map(one, range(len(sel))))
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} query rows, float64",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent, so more GPUs would each run this kernel on their share)",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_tiled_attention_23_amd as fa
+    from exact_tiled_attention_23_amd.workloads import HEADLINE, WORKLOADS, generate_workload
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {name}")
+    x = generate_workload(w)
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    kv = None if x.kv_len is None else torch.as_tensor(x.kv_len, dtype=torch.int32).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.forward(q, k, v, causal=w.causal, scale=x.scale, kv_len=kv, out=o, lse=lse, stream=stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in ev]
+    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    pairs = pair_count(w, x.kv_len)
+    flops = 4.0 * w.D * pairs
+    elt = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / avg_kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    nbytes = algorithmic_bytes(w, x.kv_len, elt)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+                "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+                "hbm_gbs_algorithmic": round(nbytes / avg_kernel_s / 1e9, 1),
+                "kernel_ms_avg": round(avg_kernel_s * 1e3, 4), "kernel_ms_min": round(min(kernel_ms), 4),
+                "kernel_ms_median": round(float(np.median(kernel_ms)), 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"bench: CPU oracle baseline on {args.cpu_heads} heads")
+        cpu = cpu_baseline(x, w, args.cpu_heads)
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "causal": w.causal,
+                       "kv_len": None if x.kv_len is None else [int(t) for t in x.kv_len],
+                       "parallelism": "single GPU"},
+            "pct_of_peak": round(100.0 * value / peak, 2),
+            "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,355 @@
+// Exact tiled attention forward with online softmax: the gfx950 kernel.
+//
+// One workgroup owns one (batch, head, query tile) ("vectorized-flash-attention-kernel",
+// Core algorithm: for each batch, head and query block, loop over key/value blocks).
+// NW waves of 64 lanes each own 32 consecutive query rows. Per key/value tile:
+//
+//   stage   K tile -> LDS row-major, V tile -> LDS transposed (V^T), from 16-byte
+//           coalesced global loads that were issued one tile ahead into registers;
+//   S^T     = K . Q^T on 32x32 MFMA (fp32 accumulate). With this orientation the
+//           accumulator layout puts one query per lane (lane % 32) and half of the
+//           tile's keys in each 32-lane half, so row statistics stay in registers;
+//   mask    causal (key > query) and padding (key >= kv_len) to -inf, only on tiles
+//           that straddle the diagonal or the kv_len edge;
+//   softmax running max m (base-2, scaled), alpha = 2^(m_old - m_new), p = 2^(s*c - m),
+//           with c = scale*log2(e); a row whose max is still -inf subtracts 0 instead,
+//           so no exp(-inf - -inf) ever happens ("js-flash-attention-tiled-online-
+//           softmax-exactness", Root causes addressed 1 and 2);
+//   O^T    = alpha*O^T + V^T . P^T on 32x32 MFMA, P taken straight from the S^T
+//           accumulator registers (K rows are loaded in a permuted order so that the
+//           accumulator layout is exactly the B-operand layout of this product).
+//
+// Tiles wholly above the causal diagonal or past kv_len are never loaded
+// ("vectorized-flash-attention-kernel", Key design decision 3). The epilogue writes
+// O = acc / l (exact zeros when l == 0) and LSE = m + ln l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Per-element-type matrix-core step. KPER: reduction elements a lane holds per
+// operand per instruction; one instruction reduces over KSTEP = 2*KPER elements
+// (lanes 0-31 hold the first KPER, lanes 32-63 the next KPER).
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  static constexpr int KPER = 8;
+  typedef __bf16 frag __attribute__((__vector_size__(8 * sizeof(__bf16))));
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<_Float16> {
+  static constexpr int KPER = 8;
+  typedef _Float16 frag __attribute__((__vector_size__(8 * sizeof(_Float16))));
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KPER = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* kv_len;  // nullable
+  int64_t H;
+  int64_t N;
+  float scale_log2;       // scale * log2(e), > 0
+  int causal;
+  int n_qtiles;           // ceil(N / BR)
+  int64_t n_units;        // B * H * n_qtiles (the grid size)
+  int xcd_groups;         // 8 when n_units % 8 == 0, else 1
+};
+
+// Key index (within a 32-key sub-tile) held by accumulator register i of lane half g.
+// The 32x32 accumulator gives register i of half g the row 8*(i/4) + 4*g + i%4; the
+// K rows are loaded permuted so that this row holds key KSTEP*(i/KPER) + KPER*g + i%KPER,
+// which makes registers [KPER*h, KPER*h + KPER) of half g exactly the P^T operand
+// (keys KSTEP*h + KPER*g + 0..KPER-1) of the h-th reduction step of P.V.
+template <int KPER>
+__device__ __forceinline__ int acc_key(int i, int g) {
+  return (2 * KPER) * (i / KPER) + KPER * g + (i % KPER);
+}
+
+// The K row that A-operand row r must hold so that the accumulator row layout above holds.
+template <int KPER>
+__device__ __forceinline__ int a_row_key(int r) {
+  return acc_key<KPER>(4 * (r / 8) + (r % 4), (r / 4) % 2);
+}
+
+template <typename T, int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPER = M::KPER;
+  constexpr int KSTEP = 2 * KPER;
+  constexpr int NT = NW * 64;
+  constexpr int BR = 32 * NW;
+  constexpr int CH = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+  constexpr int CPR = D / CH;                    // chunks per row
+  constexpr int KLD = D + CH;                    // K row stride in LDS (padded by 16 bytes)
+  constexpr int VLD = BC + CH;                   // V^T row stride in LDS
+  constexpr int NSUB = BC / 32;                  // 32-key sub-tiles per tile
+  constexpr int NDT = D / 32;                    // 32-wide output column tiles
+  constexpr int NQF = D / KSTEP;                 // Q fragments (reduction steps over D)
+  constexpr int K_UNITS = BC * CPR / NT;         // 16-byte K chunks per thread per tile
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert((BC * CPR) % NT == 0, "K staging must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) T k_lds[BC * KLD];
+  __shared__ __attribute__((aligned(16))) T vt_lds[D * VLD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;       // lane half
+  const int r = lane & 31;       // query column of this lane / A-operand row
+
+  // Work unit: heads are grouped per XCD (blocks are dispatched round-robin over the 8
+  // XCDs) so the query tiles of a head share one L2; causal runs the longest tiles first.
+  int64_t bid = blockIdx.x;
+  int64_t unit = bid;
+  if (p.xcd_groups == 8) unit = (bid % 8) * (p.n_units / 8) + bid / 8;
+  const int64_t bh = unit / p.n_qtiles;
+  int qt = (int)(unit % p.n_qtiles);
+  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const int64_t b = bh / p.H;
+  const int64_t N = p.N;
+
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + bh * N * D;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + bh * N * D;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + bh * N * D;
+  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + bh * N * D;
+  float* __restrict__ Lh = p.lse + bh * N;
+
+  const int64_t q0 = (int64_t)qt * BR;
+  const int64_t qw = q0 + 32 * wave;       // first query row of this wave
+  const int64_t qrow = qw + r;             // this lane's query row
+
+  int64_t kvl = N;
+  if (p.kv_len) {
+    int64_t x = p.kv_len[b];
+    kvl = x < 0 ? 0 : (x > N ? N : x);
+  }
+  // Keys any row of this tile may see, and keys any row of this wave may see.
+  int64_t kv_hi = kvl;
+  int64_t wave_hi = kvl;
+  if (p.causal) {
+    kv_hi = kv_hi < q0 + BR ? kv_hi : q0 + BR;
+    wave_hi = wave_hi < qw + 32 ? wave_hi : qw + 32;
+  }
+  const int ntiles = kv_hi > 0 ? (int)((kv_hi + BC - 1) / BC) : 0;
+
+  // Q^T as the B operand of S^T = K . Q^T: lane holds Q[qrow][KSTEP*s + KPER*g + 0..KPER-1].
+  frag qf[NQF];
+#pragma unroll
+  for (int s = 0; s < NQF; ++s) {
+    if (qrow < N) {
+      qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * D + KSTEP * s + KPER * g);
+    } else {
+      qf[s] = frag{};
+    }
+  }
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = f32x16{};
+  float m2 = -INFINITY;  // running max of scaled base-2 logits for this lane's query
+  float lsum = 0.f;      // this lane half's share of the running denominator
+
+  const float c = p.scale_log2;
+  const int krow_a = a_row_key<KPER>(r);
+
+  // ---- register staging of the next K/V tile
+  uint4 kreg[K_UNITS];
+  constexpr int V_UNITS = (sizeof(T) == 2) ? (BC / 2) * CPR / NT : BC * CPR / NT;
+  constexpr int V_ROWS = (sizeof(T) == 2) ? 2 : 1;
+  static_assert(((sizeof(T) == 2) ? (BC / 2) * CPR : BC * CPR) % NT == 0, "V staging must divide evenly");
+  uint4 vreg[V_UNITS][V_ROWS];
+
+  auto load_tile = [&](int64_t j0) {
+#pragma unroll
+    for (int n = 0; n < K_UNITS; ++n) {
+      const int cidx = tid + n * NT;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * CH;
+      const int64_t key = j0 + row;
+      kreg[n] = key < kv_hi ? *reinterpret_cast<const uint4*>(Kh + key * D + col) : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int n = 0; n < V_UNITS; ++n) {
+      const int cidx = tid + n * NT;
+      const int row0 = (cidx / CPR) * V_ROWS;
+      const int col = (cidx % CPR) * CH;
+#pragma unroll
+      for (int e = 0; e < V_ROWS; ++e) {
+        const int64_t key = j0 + row0 + e;
+        vreg[n][e] = key < kv_hi ? *reinterpret_cast<const uint4*>(Vh + key * D + col) : uint4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int n = 0; n < K_UNITS; ++n) {
+      const int cidx = tid + n * NT;
+      const int row = cidx / CPR;
+      const int col = (cidx % CPR) * CH;
+      *reinterpret_cast<uint4*>(&k_lds[row * KLD + col]) = kreg[n];
+    }
+#pragma unroll
+    for (int n = 0; n < V_UNITS; ++n) {
+      const int cidx = tid + n * NT;
+      const int row0 = (cidx / CPR) * V_ROWS;
+      const int col = (cidx % CPR) * CH;
+      if constexpr (sizeof(T) == 2) {
+        // Two consecutive keys per 32-bit word of V^T: word (d, row0/2) = V[row0][d] | V[row0+1][d] << 16.
+        const uint32_t a[4] = {vreg[n][0].x, vreg[n][0].y, vreg[n][0].z, vreg[n][0].w};
+        const uint32_t bb[4] = {vreg[n][1].x, vreg[n][1].y, vreg[n][1].z, vreg[n][1].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = (a[w] & 0xffffu) | (bb[w] << 16);
+          const uint32_t hi = (a[w] >> 16) | (bb[w] & 0xffff0000u);
+          *reinterpret_cast<uint32_t*>(&vt_lds[(col + 2 * w) * VLD + row0]) = lo;
+          *reinterpret_cast<uint32_t*>(&vt_lds[(col + 2 * w + 1) * VLD + row0]) = hi;
+        }
+      } else {
+        const float f[4] = {__uint_as_float(vreg[n][0].x), __uint_as_float(vreg[n][0].y),
+                            __uint_as_float(vreg[n][0].z), __uint_as_float(vreg[n][0].w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt_lds[(col + e) * VLD + row0] = f[e];
+      }
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t j0 = (int64_t)t * BC;
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();  // the tile is in LDS
+    if (t + 1 < ntiles) load_tile(j0 + BC);
+
+    if (j0 < wave_hi) {  // wave-uniform: some row of this wave sees a key of this tile
+      // ---- S^T = K . Q^T
+      f32x16 s[NSUB];
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        s[u] = f32x16{};
+        const T* arow = &k_lds[(32 * u + krow_a) * KLD + KPER * g];
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          const frag a = *reinterpret_cast<const frag*>(arow + KSTEP * st);
+          s[u] = M::run(a, qf[st], s[u]);
+        }
+      }
+
+      // ---- masks: only where the tile crosses the kv_len edge or this wave's diagonal
+      const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int64_t key = j0 + 32 * u + acc_key<KPER>(i, g);
+            const bool dead = key >= kvl || (p.causal && key > qrow);
+            if (dead) s[u][i] = -INFINITY;
+          }
+        }
+      }
+
+      // ---- online softmax (base 2)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[u][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m2, mx * c);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+      m2 = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][i], c, -m_use));
+          s[u][i] = pv;
+          lsum += pv;
+        }
+
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int kk = 0; kk < BC / KSTEP; ++kk) {
+        constexpr int STEPS_PER_SUB = 32 / KSTEP;
+        const int u = kk / STEPS_PER_SUB;
+        const int h = kk % STEPS_PER_SUB;
+        frag pf;
+        if constexpr (KPER == 1) {
+          pf = s[u][h];
+        } else {
+#pragma unroll
+          for (int e = 0; e < KPER; ++e) pf[e] = (T)s[u][h * KPER + e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const frag a = *reinterpret_cast<const frag*>(&vt_lds[(32 * dt + r) * VLD + KSTEP * kk + KPER * g]);
+          oacc[dt] = M::run(a, pf, oacc[dt]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = acc / l (0 when l == 0), LSE = (m + log2 l) * ln 2
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (qrow < N) {
+    const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * dt + 8 * a4 + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          T o4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * a4 + e] * inv);
+          *reinterpret_cast<uint2*>(Oh + qrow * D + d) = *reinterpret_cast<const uint2*>(o4);
+        } else {
+          float4 o4;
+          o4.x = oacc[dt][4 * a4 + 0] * inv;
+          o4.y = oacc[dt][4 * a4 + 1] * inv;
+          o4.z = oacc[dt][4 * a4 + 2] * inv;
+          o4.w = oacc[dt][4 * a4 + 3] * inv;
+          *reinterpret_cast<float4*>(Oh + qrow * D + d) = o4;
+        }
+      }
+    }
+    if (g == 0) Lh[qrow] = (ltot == 0.f) ? -INFINITY : (m2 + log2f(ltot)) * kLn2;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,88 @@
+/*
+ * fa.h - C ABI of the exact tiled attention forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("vectorized-flash-attention-kernel", Core algorithm; Constructor
+ * options; Key design decisions 1, 3 and 4): for every batch b, head h and query
+ * row i,
+ *
+ *     J_i   = { j : j < kv_len[b]  and  (causal == 0  or  j <= i) }
+ *     s_j   = scale * sum_d Q[b,h,i,d] * K[b,h,j,d]                  (j in J_i)
+ *     O_i   = sum_j exp(s_j - m) V[b,h,j,:] / l,  m = max_j s_j,  l = sum_j exp(s_j - m)
+ *     LSE_i = m + ln l                                               (natural log)
+ *
+ * computed tile by tile with the online-softmax recurrence (running row max and
+ * denominator, accumulator rescaled by exp(m_old - m_new)), so the N x N score
+ * matrix never reaches device memory. A row with no valid key (J_i empty) yields
+ * O_i = 0 exactly and LSE_i = -inf, never NaN
+ * ("js-flash-attention-tiled-online-softmax-exactness", Root causes addressed 2).
+ * Key padding follows "Paper: FlashAttention", Objectives, Code (hardened masking:
+ * padding, empty rows): keys at or past kv_len[b] are masked; query rows never are.
+ * The causal mask is top-left aligned: key j is visible to query i iff j <= i.
+ *
+ * Arithmetic: Q.K^T and P.V run on the matrix cores with float32 accumulation;
+ * softmax statistics are float32. For bf16/f16 inputs the probabilities P are
+ * rounded to the input type (round to nearest even) before P.V, and O is
+ * rounded to the input type on store. The float32 path keeps P in float32.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_F16 = 2 } fa_dtype;
+
+/* Return codes: 0 on success, negative on error. */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                                   */
+  FA_ERR_SHAPE = -2,       /* a negative size, or sizes whose products overflow            */
+  FA_ERR_UNSUPPORTED = -3, /* head dimension or dtype not built                            */
+  FA_ERR_ALIGN = -4,       /* Q, K, V or O not 16-byte aligned; LSE or kv_len not 4-byte   */
+  FA_ERR_ARG = -5,         /* scale not finite and positive, causal not 0/1, O aliases input */
+  FA_ERR_HIP = -6          /* the kernel launch was rejected by the HIP runtime            */
+};
+
+/*
+ * fa_fwd - attention forward, asynchronous on `stream`.
+ *
+ * Q, K, V : device pointers, contiguous [B][H][N][D] of `dtype` (read only).
+ * O       : device pointer, contiguous [B][H][N][D] of `dtype` (fully overwritten).
+ *           Must not be any of Q, K, V.
+ * LSE     : device pointer, contiguous [B][H][N] float32 (fully overwritten):
+ *           ln of the softmax denominator in units of scaled logits; -inf for a
+ *           fully masked row.
+ * B, H, N, D : sizes. D must be 64 or 128. If any of B, H, N is 0 the call does
+ *           nothing and returns FA_OK (pointers are then not inspected).
+ * scale   : softmax scale applied to Q.K^T; finite and > 0 (1/sqrt(D) is usual).
+ * causal  : 1 for the causal mask, 0 for none.
+ * kv_len  : device pointer to int32[B], valid key count per batch, or NULL for
+ *           N everywhere. Values outside [0, N] are clamped to it by the kernel.
+ * dtype   : an fa_dtype value.
+ * stream  : a hipStream_t, or NULL for the default stream.
+ *
+ * Ownership: the caller owns every buffer. The library allocates nothing, frees
+ * nothing and does not synchronise; it launches one kernel on `stream`. Every
+ * argument is validated before any HIP call. No global state: thread-safe.
+ * Device faults (for example an out-of-range pointer) surface at the caller's
+ * next synchronisation, not here.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+           int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+           const int32_t* kv_len, int dtype, void* stream);
+
+/* Static, human-readable text for a return code of fa_fwd. Never NULL. */
+const char* fa_strerror(int code);
+
+/* Version of this ABI; bumped when a signature or a semantic changes. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

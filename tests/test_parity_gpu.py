@@ -1,0 +1,204 @@
+"""GPU parity: the HIP kernel (through the C ABI) against the float64 CPU oracle.
+
+Tolerances (fixed by the target, written here): float32 inputs, max |error| <= 1e-5;
+bf16/f16 inputs, |gpu - ref| <= 2e-2 + 1e-2*|ref| elementwise. The same bound
+applies to LSE, and -inf (fully masked rows) must match exactly. Inputs come from
+the seeded generator; the oracle sees them upcast exactly to float64.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_23_amd as fa
+from exact_tiled_attention_23_amd.workloads import WORKLOADS, generate, generate_workload, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def tol(dtype):
+    return (1e-5, 0.0) if dtype == "f32" else (2e-2, 1e-2)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(x, kv_len=None, causal=None, prefill_nan=True):
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    o = torch.full_like(q, float("nan")) if prefill_nan else None
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev) if prefill_nan else None
+    kl = x.kv_len if kv_len is None else kv_len
+    o, lse = fa.forward(q, k, v, causal=x.causal if causal is None else causal, scale=x.scale,
+                        kv_len=None if kl is None else torch.as_tensor(np.asarray(kl), dtype=torch.int32),
+                        out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
+    atol, rtol = tol(dtype)
+    o = o_gpu.detach().float().cpu().double().numpy()
+    l = lse_gpu.detach().cpu().double().numpy()
+    assert not np.isnan(o).any(), f"{what}: NaN in O"
+    assert not np.isnan(l).any(), f"{what}: NaN in LSE"
+    inf_ref = np.isinf(lse_ref)
+    assert np.array_equal(np.isinf(l), inf_ref), f"{what}: fully masked rows differ"
+    assert np.array_equal(l[inf_ref], lse_ref[inf_ref]), f"{what}: LSE infinities differ"
+    eo = np.abs(o - o_ref)
+    bo = atol + rtol * np.abs(o_ref)
+    assert (eo <= bo).all(), f"{what}: O max err {eo.max():.3e} (worst excess {(eo - bo).max():.3e})"
+    fin = ~inf_ref
+    el = np.abs(l[fin] - lse_ref[fin])
+    bl = atol + rtol * np.abs(lse_ref[fin])
+    assert (el <= bl).all(), f"{what}: LSE max err {el.max() if el.size else 0:.3e}"
+    return float(eo.max(initial=0.0)), float(el.max(initial=0.0))
+
+
+SWEEP_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_sweep(dtype, D, causal):
+    """Every ragged N around the 128-row and 64-key tile edges; B=2, H=3; no padding."""
+    for N in SWEEP_N:
+        say(f"sweep dtype={dtype} D={D} causal={causal} N={N}")
+        x = generate(2, 3, N, D, dtype, causal=causal, seed=1000 + N)
+        o, lse = run_gpu(x)
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+        compare(o, lse, ro, rl, dtype, f"N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_padding(dtype, causal):
+    """Per-batch kv_len including 0, 1, a tile edge, a ragged value and N."""
+    N, D = 200, 64
+    kv = np.array([0, 1, 64, 131, 200], dtype=np.int32)
+    say(f"padding dtype={dtype} causal={causal} kv={kv.tolist()}")
+    x = generate(5, 2, N, D, dtype, causal=causal, seed=77)
+    o, lse = run_gpu(x, kv_len=kv)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal, kv_len=kv)
+    compare(o, lse, ro, rl, dtype, "padding")
+    assert (o[0] == 0).all().item() and torch.isinf(lse[0]).all().item() and (lse[0] < 0).all().item()
+
+
+def test_kv_len_device_tensor_and_clamping():
+    """A device kv_len is passed through; values outside [0, N] are clamped by the kernel."""
+    N, D = 100, 128
+    x = generate(4, 1, N, D, "bf16", causal=False, seed=78)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    say("device kv_len with out-of-range values")
+    o, lse = fa.forward(q, k, v, causal=False, scale=x.scale,
+                        kv_len=torch.tensor([-5, 0, 50, 1000], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=False,
+                              kv_len=np.array([0, 0, 50, 100]))
+    compare(o, lse, ro, rl, "bf16", "clamped kv_len")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_and_zero_inputs(dtype):
+    """N=1 attends only to itself; all-zero Q, K give the running mean of V (uniform weights)."""
+    say(f"single token dtype={dtype}")
+    x = generate(2, 2, 1, 64, dtype, causal=False, seed=79)
+    o, lse = run_gpu(x)
+    atol, _ = tol(dtype)
+    assert torch.allclose(o.float().cpu(), x.v.float(), atol=atol, rtol=0)
+    say(f"zero inputs dtype={dtype}")
+    x = generate(1, 2, 150, 128, dtype, causal=True, seed=80)
+    x.q.zero_()
+    x.k.zero_()
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True)
+    compare(o, lse, ro, rl, dtype, "zero Q,K")
+    want = torch.log(torch.arange(1, 151, dtype=torch.float64))
+    assert torch.allclose(lse.double().cpu()[0, 0], want, atol=1e-5)
+
+
+def test_large_logits_no_overflow():
+    """Logits up to about 100*D (rows of Q scaled up to x100 in f16): finite and matching."""
+    N, D = 256, 64
+    say("large logits f16")
+    x = generate(1, 2, N, D, "f16", causal=True, seed=81, q_row_scale=True)
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True)
+    assert np.abs(rl).max() > 100
+    compare(o, lse, ro, rl, "f16", "large logits")
+
+
+def test_deterministic():
+    """No atomics: two runs are bitwise identical."""
+    say("determinism bf16 N=1000")
+    x = generate(2, 2, 1000, 128, "bf16", causal=True, seed=82)
+    o1, l1 = run_gpu(x)
+    o2, l2 = run_gpu(x)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_batch_is_noop():
+    dev = torch.device("cuda:0")
+    q = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device=dev)
+    o, lse = fa.forward(q, q.clone(), q.clone())
+    assert o.shape == q.shape and lse.shape == (0, 2, 16)
+
+
+def _sample_heads_rows(w, x, rng):
+    heads = {(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)}
+    if x.kv_len is not None:
+        heads.add((int(x.meta["zero_batch"]), 0))
+        nz = [b for b in range(w.B) if x.kv_len[b] > 0]
+        if nz:
+            heads.add((min(nz, key=lambda b: x.kv_len[b]), w.H - 1))
+    rows = {0, 1, 2, 31, 32, 127, 128, w.N // 2, w.N - 2, w.N - 1}
+    if x.kv_len is not None:
+        for L in x.kv_len:
+            for r in (int(L) - 1, int(L)):
+                if 0 <= r < w.N:
+                    rows.add(r)
+    rows |= set(rng.integers(0, w.N, size=24).tolist())
+    return sorted(heads), np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_workload(name):
+    """Each named workload at full size, launched as the benchmark launches it: sampled
+    rows against the oracle, plus properties that hold at any size."""
+    w = WORKLOADS[name]
+    say(f"full-size workload {name}: generating inputs")
+    x = generate_workload(w)
+    say(f"full-size workload {name}: GPU run")
+    o, lse = run_gpu(x)
+    assert not torch.isnan(o).any().item(), "NaN (or an unwritten element) in O"
+    assert not torch.isnan(lse).any().item(), "NaN (or an unwritten element) in LSE"
+    if x.kv_len is not None:
+        zb = int(x.meta["zero_batch"])
+        assert (o[zb] == 0).all().item(), "fully masked batch must be exactly zero"
+        assert (torch.isinf(lse[zb]) & (lse[zb] < 0)).all().item(), "fully masked batch must have LSE = -inf"
+    rng = np.random.default_rng(9)
+    heads, rows = _sample_heads_rows(w, x, rng)
+    ocpu = o.float().cpu()
+    lcpu = lse.cpu()
+    for b, h in heads:
+        say(f"full-size workload {name}: oracle rows of b={b} h={h}")
+        kv = None if x.kv_len is None else x.kv_len[b:b + 1]
+        ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
+                                  to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=w.causal, kv_len=kv, rows=rows)
+        compare(ocpu[b:b + 1, h:h + 1, rows], lcpu[b:b + 1, h:h + 1, rows], ro, rl, w.dtype, f"{name} b={b} h={h}")
+    if w.causal:
+        # Causal row 0 attends only to key 0 (in every batch that has a key at all).
+        atol, _ = tol(w.dtype)
+        live = [b for b in range(w.B) if x.kv_len is None or x.kv_len[b] > 0]
+        assert torch.allclose(ocpu[live, :, 0], x.v[live, :, 0].float(), atol=atol, rtol=0)
+    say(f"full-size workload {name}: determinism")
+    o2, l2 = run_gpu(x)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
