@@ -7,12 +7,14 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
+#include "fa_fwd_mfma16.h"
 
 namespace {
 
 constexpr int kAbiVersion = 1;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
+constexpr int kWavesPerSimd = 2;  // bf16/f16 kernel: two workgroups share each CU
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
@@ -38,8 +40,13 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   p.n_units = units;
   p.xcd_groups = (units % 8 == 0) ? 8 : 1;
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>),
-                                 dim3((unsigned)units), dim3(kWaves * 64), args, 0, stream);
+  const void* fn;
+  if constexpr (sizeof(T) == 2) {
+    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, kBlockKV, kWaves, kWavesPerSimd>);
+  } else {
+    fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
+  }
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(kWaves * 64), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
