@@ -117,7 +117,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-heads", type=int, default=64,
+                    help="(batch, head) pairs the CPU oracle baseline runs; all of the headline workload by default")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, run a plain device copy of this many bytes per step "
+                         "(scale reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -132,6 +136,16 @@ def main():
     import torch
     import exact_tiled_attention_23_amd as fa
     from exact_tiled_attention_23_amd.workloads import HEADLINE, WORKLOADS, generate_workload
+
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_step": src.numel() * 4,
+                          "bytes_written_per_step": src.numel() * 4, "steps": args.warmup + args.steps}))
+        return
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]

@@ -14,14 +14,51 @@ namespace {
 constexpr int kAbiVersion = 1;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
-constexpr int kWavesPerSimd = 2;  // bf16/f16 kernel: two workgroups share each CU
+// bf16/f16 kernel tuning: waves per SIMD (two workgroups share each CU), raised issue
+// priority around the matrix-core phases, keys per tile at D = 64 and D = 128.
+#ifndef FA_WAVES_PER_SIMD
+#define FA_WAVES_PER_SIMD 2
+#endif
+#ifndef FA_MFMA_PRIO
+#define FA_MFMA_PRIO 0
+#endif
+#ifndef FA_BC_D64
+#define FA_BC_D64 128
+#endif
+#ifndef FA_BC_D128
+#define FA_BC_D128 64
+#endif
+// bf16/f16 kernel: 4 = two 4-wave groups in ping-pong over a 256-row query tile,
+// 3 = one 4-wave group over a 128-row query tile.
+#ifndef FA_KERNEL16
+#define FA_KERNEL16 3
+#endif
+// Kernel 3 shape: waves per workgroup (32 query rows each) at D = 64 and D = 128, and
+// K/V tile buffers. Eight waves share each K/V tile across 256 query rows, halving the
+// copies per flop; at D = 64 (vector-bound) two 4-wave workgroups per CU do better.
+#ifndef FA_WAVES16_D64
+#define FA_WAVES16_D64 4
+#endif
+#ifndef FA_WAVES16_D128
+#define FA_WAVES16_D128 8
+#endif
+#ifndef FA_NBUF
+#define FA_NBUF 2
+#endif
+// Kernel 3 K/V staging: 1 = global loads into registers + LDS stores, 0 = direct copies.
+#ifndef FA_REGSTAGE
+#define FA_REGSTAGE 0
+#endif
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
            float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
-  constexpr int BR = 32 * kWaves;
+  constexpr bool kPingPong = sizeof(T) == 2 && FA_KERNEL16 == 4;
+  constexpr int NW = sizeof(T) == 2 ? (D == 64 ? FA_WAVES16_D64 : FA_WAVES16_D128) : kWaves;
+  constexpr int BR = kPingPong ? 256 : 32 * NW;
+  constexpr int threads = kPingPong ? 512 : 64 * NW;
   fa::FwdParams p;
   p.q = Q;
   p.k = K;
@@ -41,12 +78,15 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   p.xcd_groups = (units % 8 == 0) ? 8 : 1;
   void* args[] = {&p};
   const void* fn;
-  if constexpr (sizeof(T) == 2) {
-    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, kBlockKV, kWaves, kWavesPerSimd>);
+  constexpr int BC = D == 64 ? FA_BC_D64 : FA_BC_D128;
+  if constexpr (kPingPong) {
+    fn = reinterpret_cast<const void*>(&fa::fwd16_pingpong_kernel<T, D, BC>);
+  } else if constexpr (sizeof(T) == 2) {
+    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, BC, NW, FA_WAVES_PER_SIMD, FA_MFMA_PRIO != 0, FA_NBUF, FA_REGSTAGE != 0>);
   } else {
     fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
   }
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(kWaves * 64), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -90,6 +130,7 @@ extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, floa
   // Element counts must fit in int64 with room: B*H*N*D and the byte offsets derived from it.
   const int64_t lim = INT64_MAX / 16;
   if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
+  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;  // row indices stay in 32 bits
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (dtype) {
     case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, s);
