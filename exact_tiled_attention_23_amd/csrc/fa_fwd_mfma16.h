@@ -298,17 +298,38 @@ void fwd16_kernel(FwdParams p) {
     }
 
     if (j0 < wave_hi) {
-      // ---- S^T = K . Q^T, with the fragments of a sub-tile read ahead of its products
+      // ---- S^T = K . Q^T. The sub-tiles' products advance together, one reduction step
+      // at a time, and the K fragments of step st+PD are read while step st's products run,
+      // so each LDS read has about four products' time (~128 cycles) to land. The order is
+      // pinned with scheduling-group barriers: left to itself the scheduler reuses one
+      // fragment register and waits on every read.
       f32x16 s[NSUB];
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+      {
+        constexpr int PD = NSUB >= 4 ? 1 : 2;
+        frag ka[PD + 1][NSUB];
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-        frag ka[NQF];
+        for (int u = 0; u < NSUB; ++u) s[u] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < NQF; ++st) ka[st] = *reinterpret_cast<const frag*>(kb + u * 32 * ROWB + koff[st]);
-        s[u] = f32x16{};
+        for (int st = 0; st < PD; ++st)
 #pragma unroll
-        for (int st = 0; st < NQF; ++st) s[u] = M::run(ka[st], qf[st], s[u]);
+          for (int u = 0; u < NSUB; ++u) ka[st][u] = *reinterpret_cast<const frag*>(kb + u * 32 * ROWB + koff[st]);
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          if (st + PD < NQF) {
+#pragma unroll
+            for (int u = 0; u < NSUB; ++u)
+              ka[(st + PD) % (PD + 1)][u] = *reinterpret_cast<const frag*>(kb + u * 32 * ROWB + koff[st + PD]);
+          }
+#pragma unroll
+          for (int u = 0; u < NSUB; ++u) s[u] = M::run(ka[st % (PD + 1)][u], qf[st], s[u]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, PD * NSUB, 0);  // DS reads of the first PD steps
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          if (st + PD < NQF) __builtin_amdgcn_sched_group_barrier(0x100, NSUB, 0);  // reads for st+PD
+          __builtin_amdgcn_sched_group_barrier(0x008, NSUB, 0);                    // products of st
+        }
       }
 
       // ---- masks (edge tiles only): key j0 + 32u + acc_key(i, g) is dead when it is at
@@ -355,6 +376,18 @@ void fwd16_kernel(FwdParams p) {
             muse = mnew;
           }
         }
+        // V^T fragments of this sub-tile, read before the exponentials so the reads land
+        // while they run (order pinned below).
+        frag va[2][NDT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const unsigned char* vp = vb + (32 * u + 16 * h) * ROWB + voff[dt];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
+            va[h][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -369,17 +402,11 @@ void fwd16_kernel(FwdParams p) {
           frag pf;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[e] = (T)x[8 * h + e];
-          frag va[NDT];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const unsigned char* vp = vb + (32 * u + 16 * h) * ROWB + voff[dt];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
-            va[dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::run(va[dt], pf, oacc[dt]);
+          for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::run(va[h][dt], pf, oacc[dt]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);  // the V^T transpose reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
       }
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
