@@ -14,51 +14,32 @@ namespace {
 constexpr int kAbiVersion = 1;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
-// bf16/f16 kernel tuning: waves per SIMD (two workgroups share each CU), raised issue
-// priority around the matrix-core phases, keys per tile at D = 64 and D = 128.
-#ifndef FA_WAVES_PER_SIMD
-#define FA_WAVES_PER_SIMD 2
-#endif
-#ifndef FA_MFMA_PRIO
-#define FA_MFMA_PRIO 0
-#endif
+// bf16/f16 kernel shape: keys per K/V tile, and waves per workgroup (32 query rows each)
+// at D = 64 and D = 128. Eight waves share each K/V tile across 256 query rows at
+// D = 128, halving the copies per flop; at D = 64 (vector-bound) two 4-wave workgroups
+// per CU do better. Two waves per SIMD in both cases.
 #ifndef FA_BC_D64
 #define FA_BC_D64 128
 #endif
 #ifndef FA_BC_D128
 #define FA_BC_D128 64
 #endif
-// bf16/f16 kernel: 4 = two 4-wave groups in ping-pong over a 256-row query tile,
-// 3 = one 4-wave group over a 128-row query tile.
-#ifndef FA_KERNEL16
-#define FA_KERNEL16 3
-#endif
-// Kernel 3 shape: waves per workgroup (32 query rows each) at D = 64 and D = 128, and
-// K/V tile buffers. Eight waves share each K/V tile across 256 query rows, halving the
-// copies per flop; at D = 64 (vector-bound) two 4-wave workgroups per CU do better.
 #ifndef FA_WAVES16_D64
 #define FA_WAVES16_D64 4
 #endif
 #ifndef FA_WAVES16_D128
 #define FA_WAVES16_D128 8
 #endif
-#ifndef FA_NBUF
-#define FA_NBUF 2
-#endif
-// Kernel 3 K/V staging: 1 = global loads into registers + LDS stores, 0 = direct copies.
-#ifndef FA_REGSTAGE
-#define FA_REGSTAGE 0
-#endif
+constexpr int kWavesPerSimd = 2;
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
            float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
-  constexpr bool kPingPong = sizeof(T) == 2 && FA_KERNEL16 == 4;
   constexpr int NW = sizeof(T) == 2 ? (D == 64 ? FA_WAVES16_D64 : FA_WAVES16_D128) : kWaves;
-  constexpr int BR = kPingPong ? 256 : 32 * NW;
-  constexpr int threads = kPingPong ? 512 : 64 * NW;
+  constexpr int BR = 32 * NW;
+  constexpr int threads = 64 * NW;
   fa::FwdParams p;
   p.q = Q;
   p.k = K;
@@ -79,10 +60,8 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   void* args[] = {&p};
   const void* fn;
   constexpr int BC = D == 64 ? FA_BC_D64 : FA_BC_D128;
-  if constexpr (kPingPong) {
-    fn = reinterpret_cast<const void*>(&fa::fwd16_pingpong_kernel<T, D, BC>);
-  } else if constexpr (sizeof(T) == 2) {
-    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, BC, NW, FA_WAVES_PER_SIMD, FA_MFMA_PRIO != 0, FA_NBUF, FA_REGSTAGE != 0>);
+  if constexpr (sizeof(T) == 2) {
+    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, BC, NW, kWavesPerSimd>);
   } else {
     fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
   }

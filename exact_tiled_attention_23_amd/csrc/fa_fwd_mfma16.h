@@ -5,8 +5,8 @@
 // laid out for the CDNA4 memory path:
 //
 //  * K and V tiles go HBM -> LDS with direct 16-byte global_load_lds transfers (no
-//    register staging), double- or triple-buffered so later tiles stream in while
-//    tile t is computed; one barrier per tile. Both tiles stay row-major in LDS with an XOR
+//    register staging), double-buffered so tile t+1 streams in while tile t is
+//    computed; one barrier per tile. Both tiles stay row-major in LDS with an XOR
 //    swizzle of 16-byte chunks, chosen so every LDS read below is free of bank
 //    conflicts.
 //  * S^T = K . Q^T on 32x32x16 MFMA: each lane owns one query (lane % 32) and half of
@@ -79,12 +79,6 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Wait until at most N vector-memory instructions of this wave are outstanding.
-template <int N> __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // XOR swizzles of the 16-byte chunk index within a row (row j of the tile).
 // K is read by 16 lanes on 16 different rows at one logical chunk; V (transpose reads)
 // by 16 lanes on 4 consecutive rows x 4 consecutive chunks.
@@ -97,7 +91,7 @@ template <int D> __device__ __forceinline__ int swz_v(int j) {
   else return 4 * ((j >> 1) & 1);
 }
 
-template <typename T, int D, int BC, int NW, int WPE, bool PRIO, int NBUF, bool REGSTAGE>
+template <typename T, int D, int BC, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
@@ -116,9 +110,8 @@ void fwd16_kernel(FwdParams p) {
   constexpr int NDT = D / 32;
   constexpr int NQF = D / 16;
   static_assert(BLOCKS % NW == 0, "tile must split evenly over waves");
-  static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[NBUF * 2 * TILEB];  // [buf][K|V][tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * TILEB];  // [buf][K|V][tile]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -197,28 +190,6 @@ void fwd16_kernel(FwdParams p) {
     }
   };
 
-  // Register staging (the alternative to direct copies): rows at or past kv_hi are
-  // staged as zeros, which also keeps padding garbage out of V.
-  uint4 kst[REGSTAGE ? LPW : 1], vst[REGSTAGE ? LPW : 1];
-  auto load_regs = [&](int j0) {
-    const unsigned char* kt = Kh + (int64_t)j0 * ROWB;
-    const unsigned char* vt = Vh + (int64_t)j0 * ROWB;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const bool live = j0 + ld_row[i] < kv_hi;
-      kst[i] = live ? *reinterpret_cast<const uint4*>(kt + ld_kb[i]) : uint4{0, 0, 0, 0};
-      vst[i] = live ? *reinterpret_cast<const uint4*>(vt + ld_vb[i]) : uint4{0, 0, 0, 0};
-    }
-  };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      unsigned char* slot = lds + buf * 2 * TILEB + (wave * LPW + i) * 1024 + lane * 16;
-      *reinterpret_cast<uint4*>(slot) = kst[i];
-      *reinterpret_cast<uint4*>(slot + TILEB) = vst[i];
-    }
-  };
-
   // ---- Q^T fragments (B operand of S^T = K . Q^T), straight from global memory.
   frag qf[NQF];
 #pragma unroll
@@ -252,50 +223,28 @@ void fwd16_kernel(FwdParams p) {
   float lsum = 0.f;        // this lane half's share of the denominator
   const float c = p.scale_log2;
 
-  if constexpr (REGSTAGE) {
-    // Tile t lives in buffer t & 1; tile t+1 is stored there at the end of iteration t
-    // from registers loaded one iteration earlier.
-    if (ntiles > 0) {
-      load_regs(0);
-      store_regs(0);
-    }
-    if (ntiles > 1) load_regs(BC);
-  } else {
-    // Tiles are copied NBUF-1 ahead: tile t lives in buffer t % NBUF.
-#pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
-      if (t < ntiles) issue_tile(t * BC, t);
-  }
+  // Tile t lives in buffer t & 1 and is copied one tile ahead.
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * BC;
-    const int buf = REGSTAGE ? (t & 1) : t % NBUF;
+    const int buf = t & 1;
     const unsigned char* kb = lds + buf * 2 * TILEB;
     const unsigned char* vb = kb + TILEB;
-    if constexpr (!REGSTAGE) {
-      // This wave's copies of tile t have landed (copies of later tiles may still fly).
-      if constexpr (NBUF == 3) {
-        if (t + 1 < ntiles) wait_vmem_le<2 * LPW>();
-        else wait_vmem();
-      } else {
-        wait_vmem();
-      }
-      if (j0 + BC > kvl) {
-        // Padding rows (key >= kv_len) of V must not carry garbage into O: zero the
-        // slots this lane filled itself.
+    wait_vmem();  // this wave's copies of tile t have landed
+    if (j0 + BC > kvl) {
+      // Padding rows (key >= kv_len) of V must not carry garbage into O: zero the slots
+      // this lane filled itself.
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-          if (j0 + ld_row[i] >= kvl) {
-            const int blk = wave * LPW + i;
-            *reinterpret_cast<uint4*>(lds + buf * 2 * TILEB + TILEB + blk * 1024 + lane * 16) = uint4{0, 0, 0, 0};
-          }
+      for (int i = 0; i < LPW; ++i) {
+        if (j0 + ld_row[i] >= kvl) {
+          const int blk = wave * LPW + i;
+          *reinterpret_cast<uint4*>(lds + buf * 2 * TILEB + TILEB + blk * 1024 + lane * 16) = uint4{0, 0, 0, 0};
         }
       }
     }
     __syncthreads();  // tile t visible to all waves; all waves are done with tile t-1
-    if constexpr (!REGSTAGE) {
-      if (t + NBUF - 1 < ntiles) issue_tile((t + NBUF - 1) * BC, (t + NBUF - 1) % NBUF);
-    }
+    if (t + 1 < ntiles) issue_tile(j0 + BC, buf ^ 1);
 
     if (j0 < wave_hi) {
       // ---- S^T = K . Q^T. The sub-tiles' products advance together, one reduction step
@@ -304,7 +253,6 @@ void fwd16_kernel(FwdParams p) {
       // pinned with scheduling-group barriers: left to itself the scheduler reuses one
       // fragment register and waits on every read.
       f32x16 s[NSUB];
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
       {
         constexpr int PD = NSUB >= 4 ? 1 : 2;
         frag ka[PD + 1][NSUB];
@@ -408,300 +356,10 @@ void fwd16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);  // the V^T transpose reads
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
-    }
-    if constexpr (REGSTAGE) {
-      if (t + 1 < ntiles) {
-        store_regs((t + 1) & 1);  // buffer of tile t-1, which every wave finished before this iteration's barrier
-        if (t + 2 < ntiles) load_regs((t + 2) * BC);
-      }
     }
   }
 
   // ---- epilogue
-  const float ltot = pair_sum(lsum);
-  if (qrow < n) {
-    const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d = 32 * dt + 8 * a4 + 4 * g;
-        T o4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * a4 + e] * inv);
-        *reinterpret_cast<uint2*>(Oh + (int64_t)qrow * D + d) = *reinterpret_cast<const uint2*>(o4);
-      }
-    if (g == 0) Lh[qrow] = (ltot == 0.f) ? -INFINITY : (mref + log2f(ltot)) * kLn2;
-  }
-}
-
-// Ping-pong variant: 8 waves in two groups of 4. Group G owns query rows
-// q0 + 128*G .. +127 (32 per wave) and both groups share every K/V tile. Each group
-// alternates a matrix-core phase, GEMM(t) = { S(t) = K(t).Q^T ; O += V(t-1).P(t-1) },
-// with a vector phase, SOFTMAX(t) = { masks, running max, rescale, P(t) = 2^(S*c - m) }.
-// Group 1 runs one phase behind group 0 and workgroup barriers separate the phases, so
-// while one group's waves keep the MFMA pipes busy the other group's waves (on the
-// same SIMDs) do their exponentials and reductions.
-//
-// Slot 2t:   group 0 GEMM(t),    group 1 SOFTMAX(t-1); group 0 issues K(t+1), V(t).
-// Slot 2t+1: group 0 SOFTMAX(t), group 1 GEMM(t);      group 0's copies land.
-// Every slot ends with a workgroup barrier. K(t) lives in buffer t&1 during slots
-// 2t..2t+1 and V(t) in buffer t&1 during slots 2t+2..2t+3, so the copies issued in
-// slot 2t only overwrite buffers whose last readers finished in slot 2t-1. Both groups
-// execute the same loop body; group 1 enters it one barrier later and skips the final
-// (empty) softmax slot, so both reach the same number of barriers (2T + 3).
-template <typename T, int D, int BC>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd16_pingpong_kernel(FwdParams p) {
-  using M = Mma<T>;
-  using frag = typename M::frag;
-  static_assert(sizeof(T) == 2, "16-bit element types only");
-  static_assert(D == 64 || D == 128, "head dimension");
-  static_assert(BC % 32 == 0, "key tile");
-  constexpr int BR = 256;
-  constexpr int ROWB = D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int TILEB = BC * ROWB;
-  constexpr int BLOCKS = TILEB / 1024;
-  constexpr int LPW = BLOCKS / 4;               // copies are issued by the 4 waves of group 0
-  constexpr int RPB = 1024 / ROWB;
-  constexpr int NSUB = BC / 32;
-  constexpr int NDT = D / 32;
-  constexpr int NQF = D / 16;
-  static_assert(BLOCKS % 4 == 0 && LPW >= 1, "tile must split evenly over group 0");
-
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * TILEB];  // K0 K1 V0 V1
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave >> 2;
-  const int lw = wave & 3;  // loader slot (group 0 waves only issue copies)
-  const int g = lane >> 5;
-  const int r = lane & 31;
-
-  int unit = blockIdx.x;
-  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
-  const int bh = unit / p.n_qtiles;
-  int qt = unit % p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
-  const int b = bh / (int)p.H;
-  const int n = (int)p.N;
-
-  const int64_t head = (int64_t)bh * n * D;
-  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const unsigned char* __restrict__ Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + head);
-  const unsigned char* __restrict__ Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + head);
-  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head;
-  float* __restrict__ Lh = p.lse + (int64_t)bh * n;
-
-  const int q0 = qt * BR;
-  const int qw = q0 + 32 * wave;  // groups are contiguous: wave w owns rows q0 + 32w ..
-  const int qrow = qw + r;
-
-  int kvl = n;
-  if (p.kv_len) {
-    const int x = p.kv_len[b];
-    kvl = x < 0 ? 0 : (x > n ? n : x);
-  }
-  int kv_hi = kvl, wave_hi = kvl;
-  if (p.causal) {
-    kv_hi = min(kv_hi, q0 + BR);
-    wave_hi = min(wave_hi, qw + 32);
-  }
-  const int T_ = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
-
-  int ld_row[LPW];
-  unsigned ld_kb[LPW], ld_vb[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = (lw * LPW + i) * RPB + lane / CPR;
-    const int pc = lane % CPR;
-    ld_row[i] = j;
-    ld_kb[i] = j * ROWB + (pc ^ swz_k<D>(j)) * 16;
-    ld_vb[i] = j * ROWB + (pc ^ swz_v<D>(j)) * 16;
-  }
-  unsigned char* const kbuf0 = lds;
-  unsigned char* const vbuf0 = lds + 2 * TILEB;
-
-  // Copy one K or V tile (rows j0 .. j0+BC-1) into an LDS buffer; rows past the tensor
-  // end read row n-1 instead (masked / zeroed later).
-  auto issue = [&](const unsigned char* src_head, const unsigned* off, int j0, unsigned char* dst) {
-    const unsigned char* src = src_head + (int64_t)j0 * ROWB;
-    const unsigned dl = lds_address(dst);
-    if (j0 + BC <= n) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) lds_copy16(src, off[i], dl + (lw * LPW + i) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int over = j0 + ld_row[i] - (n - 1);
-        const unsigned back = over > 0 ? (unsigned)over * ROWB : 0u;
-        lds_copy16(src, off[i] - back, dl + (lw * LPW + i) * 1024);
-      }
-    }
-  };
-
-  frag qf[NQF];
-#pragma unroll
-  for (int s = 0; s < NQF; ++s) {
-    if (qrow < n) qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * D + 16 * s + 8 * g);
-    else qf[s] = frag{};
-  }
-#pragma unroll
-  for (int s = 0; s < NQF; ++s) asm volatile("" ::"v"(qf[s]));
-
-  const int kr = a_row_key<8>(r);
-  const int krow = kr * ROWB;
-  const int ksw = swz_k<D>(kr);
-  const int s16 = lane & 15, s4 = s16 >> 2, sm = s16 & 3, q2 = (lane >> 4) & 1;
-  int voff[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const int c = 4 * dt + 2 * q2 + (sm >> 1);
-    voff[dt] = (8 * g + s4) * ROWB + ((c ^ swz_v<D>(s4)) * 16) + (sm & 1) * 8;
-  }
-
-  f32x16 oacc[NDT];
-#pragma unroll
-  for (int t = 0; t < NDT; ++t) oacc[t] = f32x16{};
-  f32x16 sacc[NSUB];
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u) sacc[u] = f32x16{};
-  frag pf[BC / 16];
-#pragma unroll
-  for (int kk = 0; kk < BC / 16; ++kk) pf[kk] = frag{};
-  float mref = -INFINITY;
-  float lsum = 0.f;
-  const float c = p.scale_log2;
-
-  // GEMM(t): S(t) = K(t) . Q^T (t < T_) and O += V(t-1) . P(t-1) (t >= 1).
-  auto gemm = [&](int t) {
-    const bool do_s = t < T_ && t * BC < wave_hi;
-    const bool do_pv = t >= 1 && (t - 1) * BC < wave_hi;
-    const unsigned char* kb = kbuf0 + (t & 1) * TILEB;
-    const unsigned char* vb = vbuf0 + ((t - 1) & 1) * TILEB;
-    if (do_s) {
-      constexpr int KG = NQF < 4 ? NQF : 4;  // K fragments read ahead per group
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-        sacc[u] = f32x16{};
-#pragma unroll
-        for (int s0 = 0; s0 < NQF; s0 += KG) {
-          frag ka[KG];
-#pragma unroll
-          for (int e = 0; e < KG; ++e)
-            ka[e] = *reinterpret_cast<const frag*>(kb + u * 32 * ROWB + krow + ((2 * (s0 + e) + g) ^ ksw) * 16);
-#pragma unroll
-          for (int e = 0; e < KG; ++e) sacc[u] = M::run(ka[e], qf[s0 + e], sacc[u]);
-          __builtin_amdgcn_sched_barrier(0);  // keep fragment reads from piling up ahead
-        }
-      }
-    }
-    if (do_pv) {
-#pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
-        frag va[NDT];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const unsigned char* vp = vb + (16 * kk) * ROWB + voff[dt];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
-          va[dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::run(va[dt], pf[kk], oacc[dt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // SOFTMAX(t): masks, lazily moved reference maximum, P(t) = 2^(S*c - m) in T.
-  auto softmax = [&](int t) {
-    const int j0 = t * BC;
-    if (!(t < T_ && j0 < wave_hi)) return;
-    if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw)) {
-      int lim = kvl - j0;
-      if (p.causal) lim = min(lim, qrow - j0 + 1);
-      lim -= 8 * g;
-#pragma unroll
-      for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * u + 16 * (i / 8) + (i % 8) >= lim) sacc[u][i] = -INFINITY;
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < NSUB; ++u) {
-      float a0 = fmaxf(fmaxf(sacc[u][0], sacc[u][1]), fmaxf(sacc[u][2], sacc[u][3]));
-      float a1 = fmaxf(fmaxf(sacc[u][4], sacc[u][5]), fmaxf(sacc[u][6], sacc[u][7]));
-      float a2 = fmaxf(fmaxf(sacc[u][8], sacc[u][9]), fmaxf(sacc[u][10], sacc[u][11]));
-      float a3 = fmaxf(fmaxf(sacc[u][12], sacc[u][13]), fmaxf(sacc[u][14], sacc[u][15]));
-      m = fmaxf(m, fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)));
-    }
-    const float mcand = pair_max(m) * c;
-    if (__any(mcand > mref + kRescaleSlack)) {
-      const float mnew = fmaxf(mref, mcand);
-      const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-      mref = mnew;
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    }
-    const float muse = (mref == -INFINITY) ? 0.f : mref;
-    float part = 0.f;
-#pragma unroll
-    for (int u = 0; u < NSUB; ++u) {
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][8 * h + e], c, -muse));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[u][8 * h + e + 1], c, -muse));
-          pf[2 * u + h][e] = (T)p0;
-          pf[2 * u + h][e + 1] = (T)p1;
-          a0 += p0;
-          a1 += p1;
-        }
-      }
-      part += a0 + a1;
-    }
-    lsum += part;
-  };
-
-  auto land = [&](int t) {  // this wave's copies of V(t) (and K(t+1)) have landed; zero V padding
-    wait_vmem();
-    const int j0 = t * BC;
-    if (t < T_ && j0 + BC > kvl) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        if (j0 + ld_row[i] >= kvl)
-          *reinterpret_cast<uint4*>(vbuf0 + (t & 1) * TILEB + (lw * LPW + i) * 1024 + lane * 16) =
-              uint4{0, 0, 0, 0};
-    }
-  };
-
-  if (grp == 0 && T_ > 0) issue(Kh, ld_kb, 0, kbuf0);
-  wait_vmem();
-  __syncthreads();
-  if (grp == 1) __syncthreads();  // group 1 runs one slot behind
-  for (int t = 0; t <= T_; ++t) {
-    if (grp == 0) {
-      if (t + 1 < T_) issue(Kh, ld_kb, (t + 1) * BC, kbuf0 + ((t + 1) & 1) * TILEB);
-      if (t < T_) issue(Vh, ld_vb, t * BC, vbuf0 + (t & 1) * TILEB);
-    }
-    gemm(t);
-    __syncthreads();
-    if (grp == 0 || t < T_) {
-      softmax(t);
-      if (grp == 0) land(t);
-      __syncthreads();
-    }
-  }
-
   const float ltot = pair_sum(lsum);
   if (qrow < n) {
     const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
