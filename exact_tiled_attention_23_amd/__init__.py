@@ -6,8 +6,8 @@ package is its thin binding; the library is loaded on first use and its
 absence is an error, never a fallback.
 """
 
-from .binding import (FA_BF16, FA_F16, FA_F32, fa_abi_version, fa_fwd, fa_strerror, forward,
-                      load_library)
+from .binding import (FA_BF16, FA_F16, FA_F32, fa_abi_version, fa_fwd, fa_fwd_strided, fa_strerror,
+                      forward, load_library)
 
-__all__ = ["forward", "fa_fwd", "fa_strerror", "fa_abi_version", "load_library",
+__all__ = ["forward", "fa_fwd", "fa_fwd_strided", "fa_strerror", "fa_abi_version", "load_library",
            "FA_F32", "FA_BF16", "FA_F16"]

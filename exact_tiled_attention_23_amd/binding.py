@@ -15,7 +15,7 @@ from .build import LIB
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
-EXPORTED = ("fa_fwd", "fa_strerror", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_strerror", "fa_abi_version")
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 _lib = None
@@ -33,6 +33,11 @@ def load_library():
         lib.fa_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_fwd_strided.restype = ctypes.c_int
+        lib.fa_fwd_strided.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -44,6 +49,16 @@ def load_library():
 def fa_fwd(Q, K, V, O, LSE, B, H, N, D, scale, causal, kv_len, dtype, stream):
     """Raw C call; pointers are ints (0 for NULL). Returns the C return code."""
     return load_library().fa_fwd(Q, K, V, O, LSE, B, H, N, D, scale, causal, kv_len, dtype, stream)
+
+
+def fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, stream):
+    """Raw C call with strides: None (contiguous) or 12 ints (q, k, v, o; batch, head, token)."""
+    arr = None
+    if strides is not None:
+        if len(strides) != 12:
+            raise ValueError("strides needs 12 values")
+        arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    return load_library().fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, kv_len, dtype, stream)
 
 
 def fa_strerror(code):
@@ -62,6 +77,10 @@ def _check(rc):
 def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None, stream=None):
     """Attention forward on device tensors [B, H, N, D]. Returns (o, lse).
 
+    q, k, v (and out) may be any strided views whose last dimension is contiguous,
+    e.g. a [B, N, H, D] tensor transposed to [B, H, N, D]; a zero head stride on k and v
+    shares one K/V head among all query heads.
+
     causal defaults to True and scale to 1/sqrt(D) rounded to float32, as the
     pages' constructor options do. kv_len: None, or int32-convertible values
     per batch (a CPU sequence is range-checked here and copied to the device;
@@ -74,8 +93,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError("the head dimension of q, k, v must be contiguous (stride 1)")
     B, H, N, D = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
@@ -84,8 +103,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if out.shape != q.shape or out.dtype != q.dtype or (out.stride(3) != 1 and D > 1):
+        raise ValueError("out must be shaped and typed like q, with a contiguous head dimension")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
     kv_ptr = 0
@@ -106,8 +125,10 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
     with torch.cuda.device(dev):
-        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                    B, H, N, D, float(scale), 1 if causal else 0, kv_ptr, _TORCH_DTYPE[q.dtype], handle)
+        rc = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, N, D, strides, float(scale), 1 if causal else 0, kv_ptr,
+                            _TORCH_DTYPE[q.dtype], handle)
     _check(rc)
     return out, lse

@@ -11,33 +11,31 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
-// bf16/f16 kernel shape: keys per K/V tile, and waves per workgroup (32 query rows each)
-// at D = 64 and D = 128. Eight waves share each K/V tile across 256 query rows at
-// D = 128, halving the copies per flop; at D = 64 (vector-bound) two 4-wave workgroups
-// per CU do better. Two waves per SIMD in both cases.
-#ifndef FA_BC_D64
-#define FA_BC_D64 128
-#endif
-#ifndef FA_BC_D128
-#define FA_BC_D128 64
-#endif
-#ifndef FA_WAVES16_D64
-#define FA_WAVES16_D64 4
-#endif
-#ifndef FA_WAVES16_D128
-#define FA_WAVES16_D128 8
-#endif
-constexpr int kWavesPerSimd = 2;
+// bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
+// query rows each) and waves per SIMD. Eight waves share each K/V tile across 256 query
+// rows at D = 128, halving the copies per flop; at D <= 64 (vector-bound) two 4-wave
+// workgroups per CU do better; D = 256 needs one wave per SIMD for its registers.
+template <int D> struct Shape16;
+template <> struct Shape16<32> { static constexpr int BC = 128, NW = 4, WPE = 2; };
+template <> struct Shape16<64> { static constexpr int BC = 128, NW = 4, WPE = 2; };
+template <> struct Shape16<128> { static constexpr int BC = 64, NW = 8, WPE = 2; };
+template <> struct Shape16<256> { static constexpr int BC = 64, NW = 4, WPE = 1; };
+constexpr int kMaxBC = 128;  // largest key tile: bounds the per-lane 32-bit copy offsets
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
+struct Strides {
+  int64_t q[3], k[3], v[3], o[3];  // (batch, head, token) in elements
+};
+
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
-           float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
-  constexpr int NW = sizeof(T) == 2 ? (D == 64 ? FA_WAVES16_D64 : FA_WAVES16_D128) : kWaves;
+           const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
+  constexpr bool k16 = sizeof(T) == 2;
+  constexpr int NW = k16 ? Shape16<D>::NW : kWaves;
   constexpr int BR = 32 * NW;
   constexpr int threads = 64 * NW;
   fa::FwdParams p;
@@ -47,6 +45,10 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   p.o = O;
   p.lse = LSE;
   p.kv_len = kv_len;
+  p.q_sb = st.q[0]; p.q_sh = st.q[1]; p.q_sn = st.q[2];
+  p.k_sb = st.k[0]; p.k_sh = st.k[1]; p.k_sn = st.k[2];
+  p.v_sb = st.v[0]; p.v_sh = st.v[1]; p.v_sn = st.v[2];
+  p.o_sb = st.o[0]; p.o_sh = st.o[1]; p.o_sn = st.o[2];
   p.H = H;
   p.N = N;
   p.scale_log2 = scale * fa::kLog2e;
@@ -59,9 +61,9 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   p.xcd_groups = (units % 8 == 0) ? 8 : 1;
   void* args[] = {&p};
   const void* fn;
-  constexpr int BC = D == 64 ? FA_BC_D64 : FA_BC_D128;
-  if constexpr (sizeof(T) == 2) {
-    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, BC, NW, kWavesPerSimd>);
+  if constexpr (k16) {
+    using S = Shape16<D>;
+    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE>);
   } else {
     fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
   }
@@ -71,9 +73,45 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
 
 template <typename T>
 int dispatch_d(int64_t D, const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
-               int64_t N, float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
-  if (D == 64) return launch<T, 64>(Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, stream);
-  return launch<T, 128>(Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, stream);
+               int64_t N, const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
+  switch (D) {
+    case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+    case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+    case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+    default:
+      if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+      return FA_ERR_UNSUPPORTED;
+  }
+}
+
+bool supported(int dtype, int64_t D) {
+  if (D == 32 || D == 64 || D == 128) return true;
+  return D == 256 && dtype != FA_F32;
+}
+
+// Largest element offset (b, h, n, d) of a strided tensor, or -1 on overflow.
+int64_t max_offset(int64_t B, int64_t H, int64_t N, int64_t D, const int64_t s[3]) {
+  __int128 m = (__int128)(B - 1) * s[0] + (__int128)(H - 1) * s[1] + (__int128)(N - 1) * s[2] + (D - 1);
+  return m > (__int128)(INT64_MAX / 16) ? -1 : (int64_t)m;
+}
+
+// True when no two (b, h, n, d) index the same element: sorted by stride, every dimension
+// of extent > 1 must step past everything the finer dimensions span.
+bool non_overlapping(int64_t B, int64_t H, int64_t N, int64_t D, const int64_t s[3]) {
+  int64_t ext[3] = {B, H, N}, str[3] = {s[0], s[1], s[2]};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (str[j] < str[i]) {
+        int64_t t = str[i]; str[i] = str[j]; str[j] = t;
+        t = ext[i]; ext[i] = ext[j]; ext[j] = t;
+      }
+  __int128 span = D;
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] <= 1) continue;
+    if ((__int128)str[i] < span) return false;
+    span += (__int128)str[i] * (ext[i] - 1);
+  }
+  return true;
 }
 
 }  // namespace
@@ -85,35 +123,64 @@ extern "C" const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid sizes (negative, or too large for the kernel's indexing)";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype (f32, bf16, f16)";
-    case FA_ERR_ALIGN: return "misaligned pointer (Q, K, V, O need 16 bytes; LSE and kv_len 4 bytes)";
-    case FA_ERR_ARG: return "invalid argument (scale must be finite and > 0, causal 0 or 1, O must not alias Q, K or V)";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype (f32, bf16, f16) or head dimension (32, 64, 128; 256 for bf16/f16)";
+    case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE and kv_len 4 bytes)";
+    case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, O not aliasing Q, K or V nor itself)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown error code";
+  }
+}
+
+extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                              int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
+                              const int32_t* kv_len, int dtype, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (!supported(dtype, D)) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  const int64_t lim = INT64_MAX / 16;
+  if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
+  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;  // row indices stay in 32 bits
+  // The layout is checked before the pointers (it does not depend on them).
+  Strides st;
+  if (strides) {
+    for (int i = 0; i < 12; ++i)
+      if (strides[i] < 0) return FA_ERR_ARG;
+    for (int i = 0; i < 3; ++i) {
+      st.q[i] = strides[i];
+      st.k[i] = strides[3 + i];
+      st.v[i] = strides[6 + i];
+      st.o[i] = strides[9 + i];
+    }
+  } else {
+    const int64_t c[3] = {H * N * D, N * D, D};
+    for (int i = 0; i < 3; ++i) st.q[i] = st.k[i] = st.v[i] = st.o[i] = c[i];
+  }
+  const int64_t elt = dtype == FA_F32 ? 4 : 2;
+  for (const int64_t* t : {st.q, st.k, st.v, st.o}) {
+    for (int i = 0; i < 3; ++i)
+      if ((t[i] * elt) % 16 != 0) return FA_ERR_ALIGN;
+    if (max_offset(B, H, N, D, t) < 0) return FA_ERR_SHAPE;
+  }
+  if (!non_overlapping(B, H, N, D, st.o)) return FA_ERR_ARG;
+  // Per-lane copy offsets within a key tile are 32-bit: kMaxBC rows of K or V.
+  if (st.k[2] * elt > (int64_t(1) << 31) / kMaxBC || st.v[2] * elt > (int64_t(1) << 31) / kMaxBC) return FA_ERR_SHAPE;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16)) return FA_ERR_ALIGN;
+  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4))) return FA_ERR_ALIGN;
+  if (O == Q || O == K || O == V) return FA_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
+    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
+    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
   }
 }
 
 extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
                       int64_t N, int64_t D, float scale, int causal, const int32_t* kv_len, int dtype,
                       void* stream) {
-  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
-  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
-  if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16)) return FA_ERR_ALIGN;
-  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4))) return FA_ERR_ALIGN;
-  if (O == Q || O == K || O == V) return FA_ERR_ARG;
-  // Element counts must fit in int64 with room: B*H*N*D and the byte offsets derived from it.
-  const int64_t lim = INT64_MAX / 16;
-  if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
-  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;  // row indices stay in 32 bits
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  switch (dtype) {
-    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, s);
-    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, s);
-    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, scale, causal, kv_len, s);
-  }
+  return fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, nullptr, scale, causal, kv_len, dtype, stream);
 }

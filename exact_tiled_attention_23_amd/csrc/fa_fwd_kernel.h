@@ -68,8 +68,14 @@ struct FwdParams {
   const void* k;
   const void* v;
   void* o;
-  float* lse;
+  float* lse;             // contiguous [B][H][N]
   const int32_t* kv_len;  // nullable
+  // Element strides of the batch, head and token dimensions (the head dimension D is
+  // contiguous): tensor X element (b, h, n, d) lives at X + b*x_sb + h*x_sh + n*x_sn + d.
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
   int64_t H;
   int64_t N;
   float scale_log2;       // scale * log2(e), > 0
@@ -132,13 +138,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   int qt = (int)(unit % p.n_qtiles);
   if (p.causal) qt = p.n_qtiles - 1 - qt;
   const int64_t b = bh / p.H;
+  const int64_t h = bh % p.H;
   const int64_t N = p.N;
 
-  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + bh * N * D;
-  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + bh * N * D;
-  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + bh * N * D;
-  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + bh * N * D;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const T* __restrict__ Kh = reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const T* __restrict__ Vh = reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh;
+  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
   float* __restrict__ Lh = p.lse + bh * N;
+  const int64_t qsn = p.q_sn, ksn = p.k_sn, vsn = p.v_sn, osn = p.o_sn;
 
   const int64_t q0 = (int64_t)qt * BR;
   const int64_t qw = q0 + 32 * wave;       // first query row of this wave
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
     if (qrow < N) {
-      qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * D + KSTEP * s + KPER * g);
+      qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + KSTEP * s + KPER * g);
     } else {
       qf[s] = frag{};
     }
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       const int row = cidx / CPR;
       const int col = (cidx % CPR) * CH;
       const int64_t key = j0 + row;
-      kreg[n] = key < kv_hi ? *reinterpret_cast<const uint4*>(Kh + key * D + col) : uint4{0, 0, 0, 0};
+      kreg[n] = key < kv_hi ? *reinterpret_cast<const uint4*>(Kh + key * ksn + col) : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int n = 0; n < V_UNITS; ++n) {
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < V_ROWS; ++e) {
         const int64_t key = j0 + row0 + e;
-        vreg[n][e] = key < kv_hi ? *reinterpret_cast<const uint4*>(Vh + key * D + col) : uint4{0, 0, 0, 0};
+        vreg[n][e] = key < kv_hi ? *reinterpret_cast<const uint4*>(Vh + key * vsn + col) : uint4{0, 0, 0, 0};
       }
     }
   };
@@ -337,14 +345,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
           T o4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * a4 + e] * inv);
-          *reinterpret_cast<uint2*>(Oh + qrow * D + d) = *reinterpret_cast<const uint2*>(o4);
+          *reinterpret_cast<uint2*>(Oh + qrow * osn + d) = *reinterpret_cast<const uint2*>(o4);
         } else {
           float4 o4;
           o4.x = oacc[dt][4 * a4 + 0] * inv;
           o4.y = oacc[dt][4 * a4 + 1] * inv;
           o4.z = oacc[dt][4 * a4 + 2] * inv;
           o4.w = oacc[dt][4 * a4 + 3] * inv;
-          *reinterpret_cast<float4*>(Oh + qrow * D + d) = o4;
+          *reinterpret_cast<float4*>(Oh + qrow * osn + d) = o4;
         }
       }
     }

@@ -82,13 +82,17 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
 // XOR swizzles of the 16-byte chunk index within a row (row j of the tile).
 // K is read by 16 lanes on 16 different rows at one logical chunk; V (transpose reads)
 // by 16 lanes on 4 consecutive rows x 4 consecutive chunks.
+// Bank of chunk p of row j: (j * 2D + 16 p) / 4 mod 64, so rows of 64 B (D = 32) shift by
+// 16 banks, rows of 128 B (D = 64) by 32, and rows of 256 B or more do not shift at all.
 template <int D> __device__ __forceinline__ int swz_k(int j) {
-  if constexpr (D == 128) return j & 15;
-  else return (j >> 1) & 7;
+  if constexpr (D >= 128) return j & 15;
+  else if constexpr (D == 64) return (j >> 1) & 7;
+  else return (j >> 2) & 3;
 }
 template <int D> __device__ __forceinline__ int swz_v(int j) {
-  if constexpr (D == 128) return 4 * (j & 3);
-  else return 4 * ((j >> 1) & 1);
+  if constexpr (D >= 128) return 4 * (j & 3);
+  else if constexpr (D == 64) return 4 * ((j >> 1) & 1);
+  else return 0;  // D = 32: four consecutive rows already sit in four different bank quarters
 }
 
 template <typename T, int D, int BC, int NW, int WPE>
@@ -97,7 +101,7 @@ void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   static_assert(sizeof(T) == 2, "16-bit element types only");
-  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dimension");
   static_assert(BC % 32 == 0, "key tile");
   constexpr int BR = 32 * NW;
   constexpr int ROWB = D * 2;                   // bytes per K/V row
@@ -124,14 +128,20 @@ void fwd16_kernel(FwdParams p) {
   int qt = unit % p.n_qtiles;
   if (p.causal) qt = p.n_qtiles - 1 - qt;
   const int b = bh / (int)p.H;
+  const int h = bh % (int)p.H;
   const int n = (int)p.N;
 
-  const int64_t head = (int64_t)bh * n * D;
-  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + head;
-  const unsigned char* __restrict__ Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + head);
-  const unsigned char* __restrict__ Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + head);
-  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + head;
+  const T* __restrict__ Qh = reinterpret_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const unsigned char* __restrict__ Kh =
+      reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + b * p.k_sb + h * p.k_sh);
+  const unsigned char* __restrict__ Vh =
+      reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + b * p.v_sb + h * p.v_sh);
+  T* __restrict__ Oh = reinterpret_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh;
   float* __restrict__ Lh = p.lse + (int64_t)bh * n;
+  // Token strides in bytes for K and V (per-lane copy offsets stay below 2^31: checked by
+  // the host), in elements for Q and O.
+  const unsigned ksnb = (unsigned)(p.k_sn * 2), vsnb = (unsigned)(p.v_sn * 2);
+  const int64_t qsn = p.q_sn, osn = p.o_sn;
 
   const int q0 = qt * BR;
   const int qw = q0 + 32 * wave;
@@ -159,13 +169,13 @@ void fwd16_kernel(FwdParams p) {
     const int j = (wave * LPW + i) * RPB + lane / CPR;
     const int pc = lane % CPR;
     ld_row[i] = j;
-    ld_kb[i] = j * ROWB + (pc ^ swz_k<D>(j)) * 16;
-    ld_vb[i] = j * ROWB + (pc ^ swz_v<D>(j)) * 16;
+    ld_kb[i] = j * ksnb + (pc ^ swz_k<D>(j)) * 16;
+    ld_vb[i] = j * vsnb + (pc ^ swz_v<D>(j)) * 16;
   }
 
   auto issue_tile = [&](int j0, int buf) {
-    const unsigned char* kt = Kh + (int64_t)j0 * ROWB;
-    const unsigned char* vt = Vh + (int64_t)j0 * ROWB;
+    const unsigned char* kt = Kh + (int64_t)j0 * ksnb;
+    const unsigned char* vt = Vh + (int64_t)j0 * vsnb;
     unsigned char* kb = lds + buf * 2 * TILEB;
     unsigned char* vb = kb + TILEB;
     const unsigned kl = lds_address(kb), vl = lds_address(vb);
@@ -183,9 +193,9 @@ void fwd16_kernel(FwdParams p) {
       for (int i = 0; i < LPW; ++i) {
         const int blk = wave * LPW + i;
         const int over = j0 + ld_row[i] - (n - 1);
-        const unsigned back = over > 0 ? (unsigned)over * ROWB : 0u;
-        lds_copy16(kt, ld_kb[i] - back, kl + blk * 1024);
-        lds_copy16(vt, ld_vb[i] - back, vl + blk * 1024);
+        const unsigned rows_back = over > 0 ? (unsigned)over : 0u;
+        lds_copy16(kt, ld_kb[i] - rows_back * ksnb, kl + blk * 1024);
+        lds_copy16(vt, ld_vb[i] - rows_back * vsnb, vl + blk * 1024);
       }
     }
   };
@@ -194,7 +204,7 @@ void fwd16_kernel(FwdParams p) {
   frag qf[NQF];
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
-    if (qrow < n) qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * D + 16 * s + 8 * g);
+    if (qrow < n) qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + 16 * s + 8 * g);
     else qf[s] = frag{};
   }
   // Consume the Q fragments here, so the compiler's wait for them is placed before the
@@ -371,7 +381,7 @@ void fwd16_kernel(FwdParams p) {
         T o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[dt][4 * a4 + e] * inv);
-        *reinterpret_cast<uint2*>(Oh + (int64_t)qrow * D + d) = *reinterpret_cast<const uint2*>(o4);
+        *reinterpret_cast<uint2*>(Oh + qrow * osn + d) = *reinterpret_cast<const uint2*>(o4);
       }
     if (g == 0) Lh[qrow] = (ltot == 0.f) ? -INFINITY : (mref + log2f(ltot)) * kLn2;
   }

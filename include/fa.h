@@ -42,8 +42,8 @@ enum {
   FA_ERR_NULL = -1,        /* a required pointer is NULL                                   */
   FA_ERR_SHAPE = -2,       /* a negative size, or sizes whose products overflow            */
   FA_ERR_UNSUPPORTED = -3, /* head dimension or dtype not built                            */
-  FA_ERR_ALIGN = -4,       /* Q, K, V or O not 16-byte aligned; LSE or kv_len not 4-byte   */
-  FA_ERR_ARG = -5,         /* scale not finite and positive, causal not 0/1, O aliases input */
+  FA_ERR_ALIGN = -4,       /* Q, K, V, O or a stride not 16-byte aligned; LSE/kv_len 4-byte */
+  FA_ERR_ARG = -5,         /* scale not finite and > 0, causal not 0/1, bad strides, O aliases */
   FA_ERR_HIP = -6          /* the kernel launch was rejected by the HIP runtime            */
 };
 
@@ -56,8 +56,8 @@ enum {
  * LSE     : device pointer, contiguous [B][H][N] float32 (fully overwritten):
  *           ln of the softmax denominator in units of scaled logits; -inf for a
  *           fully masked row.
- * B, H, N, D : sizes. D must be 64 or 128. If any of B, H, N is 0 the call does
- *           nothing and returns FA_OK (pointers are then not inspected).
+ * B, H, N, D : sizes. D must be 32, 64 or 128 (or 256 for bf16/f16). If any of B, H,
+ *           N is 0 the call does nothing and returns FA_OK (pointers are then not inspected).
  * scale   : softmax scale applied to Q.K^T; finite and > 0 (1/sqrt(D) is usual).
  * causal  : 1 for the causal mask, 0 for none.
  * kv_len  : device pointer to int32[B], valid key count per batch, or NULL for
@@ -74,6 +74,27 @@ enum {
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
            const int32_t* kv_len, int dtype, void* stream);
+
+/*
+ * fa_fwd_strided - fa_fwd over strided Q, K, V and O. The pages' forward takes flat
+ * contiguous arrays ("vectorized-flash-attention-kernel", Core algorithm); this entry point
+ * accepts the strided views callers usually hold (for example [B][N][H][D] storage seen as
+ * [B][H][N][D]) without a copy. The arithmetic is that of fa_fwd.
+ *
+ * strides : host pointer to 12 int64 element strides, or NULL for contiguous [B][H][N][D]:
+ *           { q_b, q_h, q_n,  k_b, k_h, k_n,  v_b, v_h, v_n,  o_b, o_h, o_n }.
+ *           Element (b, h, n, d) of X lives at X + b*x_b + h*x_h + n*x_n + d: the head
+ *           dimension is contiguous. Every stride must be >= 0 and a multiple of 16 bytes.
+ *           Q, K and V may overlap themselves (a stride of 0 shares one K/V head among all
+ *           query heads); O must not (no two (b, h, n, d) may name the same element).
+ *           K and V token strides may not exceed 16 MiB. LSE stays contiguous [B][H][N].
+ * D       : 32, 64 or 128 for every dtype; 256 for FA_BF16 and FA_F16.
+ * Other arguments, ownership and errors as fa_fwd; a negative stride or an overlapping O
+ * gives FA_ERR_ARG, a misaligned stride FA_ERR_ALIGN.
+ */
+int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
+                   float scale, int causal, const int32_t* kv_len, int dtype, void* stream);
 
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -56,9 +56,13 @@ def test_negative_sizes(field):
     assert call(**{field: -1}) == binding.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("D", [0, 16, 32, 96, 100, 256])
+@pytest.mark.parametrize("D", [0, 16, 48, 96, 100, 512])
 def test_unsupported_head_dim(D):
     assert call(D=D) == binding.FA_ERR_UNSUPPORTED
+
+
+def test_head_dim_256_is_16_bit_only():
+    assert call(D=256, dtype=fa.FA_F32) == binding.FA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("dtype", [-1, 3, 7])
@@ -110,3 +114,66 @@ def test_forward_rejects_host_tensors():
         fa.forward(q, q, q)
     with pytest.raises(TypeError):
         fa.forward(q, q.float(), q)
+
+
+# ---------------------------------------------------------------- fa_fwd_strided validation
+B_, H_, N_, D_ = 2, 3, 8, 64
+CONTIG = [H_ * N_ * D_, N_ * D_, D_] * 4
+
+
+def call_strided(strides, dtype=None, **kw):
+    a = dict(GOOD, B=B_, H=H_, N=N_, D=D_)
+    a.update(kw)
+    return fa.fa_fwd_strided(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["D"], strides,
+                             a["scale"], a["causal"], a["kv_len"], a["dtype"] if dtype is None else dtype, a["stream"])
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_negative_stride(i):
+    s = list(CONTIG)
+    s[i] = -s[i]
+    assert call_strided(s) == binding.FA_ERR_ARG
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_misaligned_stride(i):
+    s = list(CONTIG)
+    s[i] += 4          # 8 bytes for bf16: not a multiple of 16
+    assert call_strided(s) == binding.FA_ERR_ALIGN
+
+
+def test_overlapping_output_rejected():
+    s = list(CONTIG)
+    s[11] = D_ // 2    # O token stride shorter than a row: rows overlap
+    assert call_strided(s) == binding.FA_ERR_ARG
+    s = list(CONTIG)
+    s[10] = 0          # two heads write the same rows
+    assert call_strided(s) == binding.FA_ERR_ARG
+
+
+def test_shared_kv_head_is_not_rejected_by_validation():
+    """A zero head stride on K and V (one K/V head for every query head) passes the layout
+    checks, which come before the pointer checks: a NULL O then stops the call."""
+    s = list(CONTIG)
+    s[4] = 0
+    s[7] = 0
+    assert call_strided(s, O=0) == binding.FA_ERR_NULL
+
+
+def test_huge_kv_token_stride():
+    s = list(CONTIG)
+    s[5] = (1 << 24)   # 32 MiB per K row in bf16
+    assert call_strided(s) == binding.FA_ERR_SHAPE
+
+
+def test_non_overlap_rule():
+    """Valid O layouts pass the layout checks (and stop at the NULL O); overlapping ones
+    are rejected before it."""
+    ok = [[H_ * N_ * D_, N_ * D_, D_],            # [B, H, N, D]
+          [N_ * H_ * D_, D_, H_ * D_],            # [B, N, H, D] seen as [B, H, N, D]
+          [H_ * N_ * 2 * D_, N_ * 2 * D_, 2 * D_]]  # padded rows
+    bad = [[H_ * N_ * D_, N_ * D_, D_ // 2], [0, N_ * D_, D_]]
+    for o in ok:
+        assert call_strided(CONTIG[:9] + o, O=0) == binding.FA_ERR_NULL
+    for o in bad:
+        assert call_strided(CONTIG[:9] + o) == binding.FA_ERR_ARG

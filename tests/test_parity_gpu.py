@@ -227,3 +227,82 @@ def test_full_size_workload(name):
     say(f"full-size workload {name}: determinism")
     o2, l2 = run_gpu(x)
     assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+# ---------------------------------------------------------------- head dimensions 32 and 256
+@pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 32), ("f16", 32), ("bf16", 256), ("f16", 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_other_head_dims(dtype, D, causal):
+    """Ragged N around the tile edges for D = 32 and D = 256, with and without padding."""
+    for N in (1, 17, 64, 129, 300):
+        say(f"head dim dtype={dtype} D={D} causal={causal} N={N}")
+        x = generate(3, 2, N, D, dtype, causal=causal, seed=2000 + N + D)
+        kv = np.array([N, max(N - 5, 0), 0], dtype=np.int32)
+        o, lse = run_gpu(x, kv_len=kv)
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal, kv_len=kv)
+        compare(o, lse, ro, rl, dtype, f"D={D} N={N}")
+
+
+# ---------------------------------------------------------------- strided layouts
+def _strided_run(x, q, k, v, out, causal, kv=None):
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=x.scale, out=out, lse=lse,
+                        kv_len=None if kv is None else torch.as_tensor(kv, dtype=torch.int32))
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 64), ("bf16", 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bnhd_layout(dtype, D, causal):
+    """[B, N, H, D] storage seen as [B, H, N, D] (token stride H*D, head stride D), for
+    Q, K, V and O alike."""
+    B, H, N = 2, 3, 200
+    say(f"BNHD layout dtype={dtype} D={D} causal={causal}")
+    x = generate(B, H, N, D, dtype, causal=causal, seed=3000 + D)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (x.q, x.k, x.v))
+    assert q.stride() == (N * H * D, D, H * D, 1)
+    out = torch.full((B, N, H, D), float("nan"), dtype=q.dtype, device=dev).transpose(1, 2)
+    o, lse = _strided_run(x, q, k, v, out, causal)
+    assert o.data_ptr() == out.data_ptr()
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+    compare(o, lse, ro, rl, dtype, "BNHD")
+
+
+def test_padded_rows_and_offset_views():
+    """Rows padded to twice their length (token stride 2D) and views that start mid-buffer."""
+    B, H, N, D = 2, 2, 150, 64
+    say("padded rows")
+    x = generate(B, H, N, D, "bf16", causal=True, seed=3100)
+    dev = torch.device("cuda:0")
+
+    def padded(t, shift):
+        buf = torch.zeros(B, H, N, 2 * D, dtype=t.dtype, device=dev)
+        buf[..., shift:shift + D] = t.to(dev)
+        return buf[..., shift:shift + D]
+
+    q, k, v = padded(x.q, 0), padded(x.k, D), padded(x.v, 8)
+    out = torch.full((B, H, N, 2 * D), float("nan"), dtype=q.dtype, device=dev)[..., D:]
+    o, lse = _strided_run(x, q, k, v, out, True)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True)
+    compare(o, lse, ro, rl, "bf16", "padded rows")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shared_kv_head(dtype):
+    """One K/V head shared by every query head (head stride 0 on K and V)."""
+    B, H, N, D = 2, 4, 180, 128 if dtype == "bf16" else 64
+    say(f"shared K/V head dtype={dtype}")
+    x = generate(B, H, N, D, dtype, causal=True, seed=3200)
+    dev = torch.device("cuda:0")
+    k1, v1 = x.k[:, :1].contiguous(), x.v[:, :1].contiguous()
+    k = k1.to(dev).expand(B, H, N, D)
+    v = v1.to(dev).expand(B, H, N, D)
+    assert k.stride(1) == 0
+    q = x.q.to(dev)
+    kv = np.array([N, 77], dtype=np.int32)
+    o, lse = _strided_run(x, q, k, v, None, True, kv)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(k1.expand(B, H, N, D)), to_f64(v1.expand(B, H, N, D)),
+                              x.scale, causal=True, kv_len=kv)
+    compare(o, lse, ro, rl, dtype, "shared K/V head")
