@@ -29,7 +29,7 @@ METRIC = "attn fwd TFLOP/s and % bf16 MFMA peak, B2 H32 N8192 D128 bf16"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_tiled_attention_23_amd/csrc/fa_fwd_kernel.h", "exact_tiled_attention_23_amd/csrc/fa_fwd_mfma16.h",
-                  "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
+                  "exact_tiled_attention_23_amd/csrc/fa_merge.h", "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -15,7 +15,9 @@ from .build import LIB
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
-EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_strerror", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_merge_states",
+            "fa_strerror", "fa_abi_version")
+MAX_SPLITS = 256
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 _lib = None
@@ -38,6 +40,18 @@ def load_library():
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_int64
+        lib.fa_fwd_split_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+        lib.fa_fwd_split.restype = ctypes.c_int
+        lib.fa_fwd_split.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_merge_states.restype = ctypes.c_int
+        lib.fa_merge_states.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -53,12 +67,35 @@ def fa_fwd(Q, K, V, O, LSE, B, H, N, D, scale, causal, kv_len, dtype, stream):
 
 def fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, stream):
     """Raw C call with strides: None (contiguous) or 12 ints (q, k, v, o; batch, head, token)."""
-    arr = None
-    if strides is not None:
-        if len(strides) != 12:
-            raise ValueError("strides needs 12 values")
-        arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    arr = _int64_array(strides, 12, "strides")
     return load_library().fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, kv_len, dtype, stream)
+
+
+def _int64_array(values, n, what):
+    if values is None:
+        return None
+    if len(values) != n:
+        raise ValueError(f"{what} needs {n} values")
+    return (ctypes.c_int64 * n)(*[int(x) for x in values])
+
+
+def fa_fwd_split_workspace_bytes(B, H, N, D, n_splits):
+    """Workspace bytes fa_fwd_split needs (0 for n_splits == 1, -1 for invalid sizes)."""
+    return load_library().fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
+
+
+def fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, n_splits, workspace,
+                 workspace_bytes, stream):
+    """Raw C call of the key-split forward; strides as fa_fwd_strided, workspace a device pointer."""
+    arr = _int64_array(strides, 12, "strides")
+    return load_library().fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, kv_len, dtype, n_splits,
+                                       workspace, workspace_bytes, stream)
+
+
+def fa_merge_states(part_o, part_lse, n_states, B, H, N, D, O, o_strides, LSE, dtype, stream):
+    """Raw C call of the partial-state merge; o_strides None (contiguous) or 3 ints (b, h, n)."""
+    arr = _int64_array(o_strides, 3, "o_strides")
+    return load_library().fa_merge_states(part_o, part_lse, n_states, B, H, N, D, O, arr, LSE, dtype, stream)
 
 
 def fa_strerror(code):
@@ -71,10 +108,17 @@ def fa_abi_version():
 
 def _check(rc):
     if rc != FA_OK:
-        raise RuntimeError(f"fa_fwd failed ({rc}): {fa_strerror(rc)}")
+        raise RuntimeError(f"attention call failed ({rc}): {fa_strerror(rc)}")
 
 
-def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None, stream=None):
+def _stream_handle(stream, dev):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None, stream=None, n_splits=1,
+            workspace=None):
     """Attention forward on device tensors [B, H, N, D]. Returns (o, lse).
 
     q, k, v (and out) may be any strided views whose last dimension is contiguous,
@@ -85,6 +129,11 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     pages' constructor options do. kv_len: None, or int32-convertible values
     per batch (a CPU sequence is range-checked here and copied to the device;
     a device int32 tensor is passed through and clamped to [0, N] by the kernel).
+
+    n_splits > 1 cuts every query tile's keys into that many parts processed by separate
+    workgroups, then merges the partial states (fa_fwd_split). workspace: None (a uint8
+    device tensor is allocated) or a device tensor of at least
+    fa_fwd_split_workspace_bytes(B, H, N, D, n_splits) bytes, 256-byte aligned.
     """
     if q.dtype not in _TORCH_DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype among float32, bfloat16, float16")
@@ -122,13 +171,51 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
                 raise ValueError("kv_len values must lie in [0, N]")
             kv_dev = kv_cpu.to(torch.int32).to(dev)
         kv_ptr = kv_dev.data_ptr()
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, dev)
     strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, strides,
+            float(scale), 1 if causal else 0, kv_ptr, _TORCH_DTYPE[q.dtype])
     with torch.cuda.device(dev):
-        rc = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                            B, H, N, D, strides, float(scale), 1 if causal else 0, kv_ptr,
-                            _TORCH_DTYPE[q.dtype], handle)
+        if n_splits == 1 and workspace is None:
+            rc = fa_fwd_strided(*args, handle)
+        else:
+            need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
+            if need < 0:
+                raise ValueError(f"n_splits must lie in [1, {MAX_SPLITS}] (got {n_splits})")
+            if workspace is None:
+                workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            if not workspace.is_cuda or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous device tensor")
+            ws_bytes = workspace.numel() * workspace.element_size()
+            rc = fa_fwd_split(*args, n_splits, workspace.data_ptr(), ws_bytes, handle)
+    _check(rc)
+    return out, lse
+
+
+def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=None):
+    """Merge S partial states: part_o float32 [S, B, H, N, D], part_lse float32 [S, B, H, N]
+    (both contiguous, on the device). Returns (o, lse) with o of `dtype` (default float32)."""
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("part_o and part_lse must be float32")
+    if part_o.dim() != 5 or part_lse.shape != part_o.shape[:4]:
+        raise ValueError("part_o must be [S, B, H, N, D] and part_lse [S, B, H, N]")
+    if not (part_o.is_cuda and part_lse.is_cuda and part_o.is_contiguous() and part_lse.is_contiguous()):
+        raise ValueError("part_o and part_lse must be contiguous device tensors")
+    S, B, H, N, D = part_o.shape
+    dev = part_o.device
+    dtype = torch.float32 if dtype is None else dtype
+    if dtype not in _TORCH_DTYPE:
+        raise TypeError("dtype must be float32, bfloat16 or float16")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if out.shape != (B, H, N, D) or out.dtype != dtype or (out.stride(3) != 1 and D > 1):
+        raise ValueError("out must be [B, H, N, D] of dtype with a contiguous last dimension")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
+    with torch.cuda.device(dev):
+        rc = fa_merge_states(part_o.data_ptr(), part_lse.data_ptr(), S, B, H, N, D, out.data_ptr(),
+                             list(out.stride()[:3]), lse.data_ptr(), _TORCH_DTYPE[dtype], _stream_handle(stream, dev))
     _check(rc)
     return out, lse

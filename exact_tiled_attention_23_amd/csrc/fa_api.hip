@@ -8,10 +8,11 @@
 #include "fa.h"
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_mfma16.h"
+#include "fa_merge.h"
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
 // bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
@@ -31,9 +32,17 @@ struct Strides {
   int64_t q[3], k[3], v[3], o[3];  // (batch, head, token) in elements
 };
 
+// Key-axis split of the forward: n partial states written to part_o / part_lse.
+struct Split {
+  int n = 1;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+};
+
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
-           const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
+           const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream,
+           const Split& sp = Split()) {
   constexpr bool k16 = sizeof(T) == 2;
   constexpr int NW = k16 ? Shape16<D>::NW : kWaves;
   constexpr int BR = 32 * NW;
@@ -54,11 +63,15 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   p.scale_log2 = scale * fa::kLog2e;
   p.causal = causal;
   const int64_t n_qtiles = (N + BR - 1) / BR;
-  const int64_t units = B * H * n_qtiles;
+  const int64_t units = B * H * n_qtiles * sp.n;
   if (n_qtiles > INT32_MAX || units > INT32_MAX) return FA_ERR_SHAPE;
   p.n_qtiles = (int)n_qtiles;
   p.n_units = units;
   p.xcd_groups = (units % 8 == 0) ? 8 : 1;
+  p.n_splits = sp.n;
+  p.BH = B * H;
+  p.part_o = sp.part_o;
+  p.part_lse = sp.part_lse;
   void* args[] = {&p};
   const void* fn;
   if constexpr (k16) {
@@ -73,16 +86,59 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
 
 template <typename T>
 int dispatch_d(int64_t D, const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
-               int64_t N, const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream) {
+               int64_t N, const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream,
+               const Split& sp = Split()) {
   switch (D) {
-    case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
-    case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
-    case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+    case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+    case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+    case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
     default:
-      if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream);
+      if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
       return FA_ERR_UNSUPPORTED;
   }
 }
+
+template <typename T, int D>
+int launch_merge(const float* part_o, const float* part_lse, int S, int64_t B, int64_t H, int64_t N, void* O,
+                 const int64_t o_st[3], float* LSE, hipStream_t stream) {
+  fa::MergeParams m;
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.n_states = S;
+  m.rows = B * H * N;
+  m.H = H;
+  m.N = N;
+  m.o = O;
+  m.o_sb = o_st[0];
+  m.o_sh = o_st[1];
+  m.o_sn = o_st[2];
+  m.lse = LSE;
+  constexpr int rows_per_block = 256 / (D / 4);
+  const int64_t blocks = (m.rows + rows_per_block - 1) / rows_per_block;
+  if (blocks > INT32_MAX) return FA_ERR_SHAPE;
+  void* args[] = {&m};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::merge_kernel<T, D>), dim3((unsigned)blocks),
+                                 dim3(256), args, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T>
+int dispatch_merge(int64_t D, const float* part_o, const float* part_lse, int S, int64_t B, int64_t H, int64_t N,
+                   void* O, const int64_t o_st[3], float* LSE, hipStream_t stream) {
+  switch (D) {
+    case 32: return launch_merge<T, 32>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
+    case 64: return launch_merge<T, 64>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
+    case 128: return launch_merge<T, 128>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
+    default: return launch_merge<T, 256>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
+  }
+}
+
+constexpr int kMaxSplits = 256;
+
+// Workspace of a split forward: S*B*H*N*D floats of partial O, then (256-byte aligned)
+// S*B*H*N floats of partial LSE.
+int64_t part_o_bytes(int64_t S, int64_t BHN, int64_t D) { return ((S * BHN * D * 4 + 255) / 256) * 256; }
+int64_t split_workspace(int64_t S, int64_t BHN, int64_t D) { return part_o_bytes(S, BHN, D) + S * BHN * 4; }
 
 bool supported(int dtype, int64_t D) {
   if (D == 32 || D == 64 || D == 128) return true;
@@ -131,20 +187,27 @@ extern "C" const char* fa_strerror(int code) {
   }
 }
 
-extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
-                              int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
-                              const int32_t* kv_len, int dtype, void* stream) {
+namespace {
+
+// Checks shared by every forward entry point. Returns FA_OK and fills st, or an error;
+// *empty is set when there is nothing to compute (then nothing else is inspected).
+int validate_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
+                     int64_t N, int64_t D, const int64_t* strides, float scale, int causal, const int32_t* kv_len,
+                     int dtype, Strides& st, bool* empty) {
+  *empty = false;
   if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
   if (!supported(dtype, D)) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
   const int64_t lim = INT64_MAX / 16;
   if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
   if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;  // row indices stay in 32 bits
   // The layout is checked before the pointers (it does not depend on them).
-  Strides st;
   if (strides) {
     for (int i = 0; i < 12; ++i)
       if (strides[i] < 0) return FA_ERR_ARG;
@@ -171,12 +234,99 @@ extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void*
   if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16)) return FA_ERR_ALIGN;
   if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4))) return FA_ERR_ALIGN;
   if (O == Q || O == K || O == V) return FA_ERR_ARG;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return FA_OK;
+}
+
+int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
+                int64_t D, const Strides& st, float scale, int causal, const int32_t* kv_len, int dtype,
+                hipStream_t s, const Split& sp) {
   switch (dtype) {
-    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
-    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
-    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s);
+    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
+    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
+    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
   }
+}
+
+int run_merge(const float* part_o, const float* part_lse, int S, int64_t B, int64_t H, int64_t N, int64_t D,
+              void* O, const int64_t o_st[3], float* LSE, int dtype, hipStream_t s) {
+  switch (dtype) {
+    case FA_BF16: return dispatch_merge<__bf16>(D, part_o, part_lse, S, B, H, N, O, o_st, LSE, s);
+    case FA_F16: return dispatch_merge<_Float16>(D, part_o, part_lse, S, B, H, N, O, o_st, LSE, s);
+    default: return dispatch_merge<float>(D, part_o, part_lse, S, B, H, N, O, o_st, LSE, s);
+  }
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                              int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
+                              const int32_t* kv_len, int dtype, void* stream) {
+  Strides st;
+  bool empty;
+  const int rc = validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, st, &empty);
+  if (rc != FA_OK || empty) return rc;
+  return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype,
+                     reinterpret_cast<hipStream_t>(stream), Split());
+}
+
+extern "C" int64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int n_splits) {
+  if (B < 0 || H < 0 || N < 0 || D < 0 || n_splits < 1 || n_splits > kMaxSplits) return -1;
+  if (n_splits == 1) return 0;
+  const int64_t lim = INT64_MAX / 1024;
+  if ((H && B > lim / H) || (N && B * H > lim / N) || (D && B * H * N > lim / D / kMaxSplits)) return -1;
+  return split_workspace(n_splits, B * H * N, D);
+}
+
+extern "C" int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                            int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
+                            const int32_t* kv_len, int dtype, int n_splits, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_ARG;
+  Strides st;
+  bool empty;
+  int rc = validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, st, &empty);
+  if (rc != FA_OK || empty) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (n_splits == 1) return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype, s, Split());
+  const int64_t need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits);
+  if (need < 0) return FA_ERR_SHAPE;
+  if (!workspace) return FA_ERR_NULL;
+  if (misaligned(workspace, 256)) return FA_ERR_ALIGN;
+  if (workspace_bytes < need) return FA_ERR_ARG;
+  Split sp;
+  sp.n = n_splits;
+  sp.part_o = static_cast<float*>(workspace);
+  sp.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(n_splits, B * H * N, D));
+  rc = run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype, s, sp);
+  if (rc != FA_OK) return rc;
+  return run_merge(sp.part_o, sp.part_lse, n_splits, B, H, N, D, O, st.o, LSE, dtype, s);
+}
+
+extern "C" int fa_merge_states(const float* part_o, const float* part_lse, int n_states, int64_t B, int64_t H,
+                               int64_t N, int64_t D, void* O, const int64_t* o_strides, float* LSE, int dtype,
+                               void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (n_states < 1 || n_states > kMaxSplits) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  const int64_t lim = INT64_MAX / 1024;
+  if (B > lim / H || B * H > lim / N || B * H * N > lim / D / kMaxSplits) return FA_ERR_SHAPE;
+  int64_t o_st[3] = {H * N * D, N * D, D};
+  if (o_strides) {
+    for (int i = 0; i < 3; ++i) {
+      if (o_strides[i] < 0) return FA_ERR_ARG;
+      o_st[i] = o_strides[i];
+    }
+  }
+  const int64_t elt = dtype == FA_F32 ? 4 : 2;
+  for (int i = 0; i < 3; ++i)
+    if ((o_st[i] * elt) % 16 != 0) return FA_ERR_ALIGN;
+  if (max_offset(B, H, N, D, o_st) < 0) return FA_ERR_SHAPE;
+  if (!non_overlapping(B, H, N, D, o_st)) return FA_ERR_ARG;
+  if (!part_o || !part_lse || !O || !LSE) return FA_ERR_NULL;
+  if (misaligned(part_o, 16) || misaligned(part_lse, 4) || misaligned(O, 16) || misaligned(LSE, 4)) return FA_ERR_ALIGN;
+  return run_merge(part_o, part_lse, n_states, B, H, N, D, O, o_st, LSE, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,

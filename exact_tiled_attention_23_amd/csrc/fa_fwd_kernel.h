@@ -81,9 +81,36 @@ struct FwdParams {
   float scale_log2;       // scale * log2(e), > 0
   int causal;
   int n_qtiles;           // ceil(N / BR)
-  int64_t n_units;        // B * H * n_qtiles (the grid size)
+  int64_t n_units;        // B * H * n_qtiles * n_splits (the grid size)
   int xcd_groups;         // 8 when n_units % 8 == 0, else 1
+  // Key-axis split: with n_splits > 1 the work unit also names a split s. A query tile
+  // with T visible key tiles gives split s the tiles [s*c, min(T, (s+1)*c)), c = ceil(T/S),
+  // and the epilogue stores that split's normalised partial state (O_s in float32, LSE_s)
+  // to part_o [S][B*H][N][D] and part_lse [S][B*H][N] instead of O and LSE.
+  int n_splits;
+  int64_t BH;
+  float* part_o;
+  float* part_lse;
 };
+
+// Work unit -> (bh, query tile, split). Heads are grouped per XCD (blocks are dispatched
+// round-robin over the 8 XCDs) so the query tiles of a head share one L2; causal runs the
+// longest query tiles first.
+struct Unit {
+  int bh, qt, split;
+};
+__device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
+  int unit = bid;
+  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
+  Unit u;
+  const int per_head = p.n_qtiles * p.n_splits;
+  u.bh = unit / per_head;
+  const int rem = unit % per_head;
+  u.qt = rem / p.n_splits;
+  u.split = rem % p.n_splits;
+  if (p.causal) u.qt = p.n_qtiles - 1 - u.qt;
+  return u;
+}
 
 // Key index (within a 32-key sub-tile) held by accumulator register i of lane half g.
 // The 32x32 accumulator gives register i of half g the row 8*(i/4) + 4*g + i%4; the
@@ -129,14 +156,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int g = lane >> 5;       // lane half
   const int r = lane & 31;       // query column of this lane / A-operand row
 
-  // Work unit: heads are grouped per XCD (blocks are dispatched round-robin over the 8
-  // XCDs) so the query tiles of a head share one L2; causal runs the longest tiles first.
-  int64_t bid = blockIdx.x;
-  int64_t unit = bid;
-  if (p.xcd_groups == 8) unit = (bid % 8) * (p.n_units / 8) + bid / 8;
-  const int64_t bh = unit / p.n_qtiles;
-  int qt = (int)(unit % p.n_qtiles);
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const Unit wu = decode_unit(p, blockIdx.x);
+  const int64_t bh = wu.bh;
+  const int qt = wu.qt;
   const int64_t b = bh / p.H;
   const int64_t h = bh % p.H;
   const int64_t N = p.N;
@@ -164,7 +186,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     kv_hi = kv_hi < q0 + BR ? kv_hi : q0 + BR;
     wave_hi = wave_hi < qw + 32 ? wave_hi : qw + 32;
   }
-  const int ntiles = kv_hi > 0 ? (int)((kv_hi + BC - 1) / BC) : 0;
+  // Key tiles [t_lo, t_hi) of this unit's split.
+  const int all_tiles = kv_hi > 0 ? (int)((kv_hi + BC - 1) / BC) : 0;
+  const int chunk = (all_tiles + p.n_splits - 1) / p.n_splits;
+  const int t_lo = min(all_tiles, wu.split * chunk);
+  const int t_hi = min(all_tiles, t_lo + chunk);
 
   // Q^T as the B operand of S^T = K . Q^T: lane holds Q[qrow][KSTEP*s + KPER*g + 0..KPER-1].
   frag qf[NQF];
@@ -248,14 +274,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     }
   };
 
-  if (ntiles > 0) load_tile(0);
+  if (t_lo < t_hi) load_tile((int64_t)t_lo * BC);
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < t_hi; ++t) {
     const int64_t j0 = (int64_t)t * BC;
     __syncthreads();  // every wave is done reading the previous tile
     store_tile();
     __syncthreads();  // the tile is in LDS
-    if (t + 1 < ntiles) load_tile(j0 + BC);
+    if (t + 1 < t_hi) load_tile(j0 + BC);
 
     if (j0 < wave_hi) {  // wave-uniform: some row of this wave sees a key of this tile
       // ---- S^T = K . Q^T
@@ -334,6 +360,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   // ---- epilogue: O = acc / l (0 when l == 0), LSE = (m + log2 l) * ln 2
   const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (p.n_splits > 1) {
+    if (qrow < N) {
+      const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
+      const int64_t prow = ((int64_t)wu.split * p.BH + bh) * N + qrow;
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          float4 o4;
+          o4.x = oacc[dt][4 * a4 + 0] * inv;
+          o4.y = oacc[dt][4 * a4 + 1] * inv;
+          o4.z = oacc[dt][4 * a4 + 2] * inv;
+          o4.w = oacc[dt][4 * a4 + 3] * inv;
+          *reinterpret_cast<float4*>(po + 32 * dt + 8 * a4 + 4 * g) = o4;
+        }
+      if (g == 0) p.part_lse[prow] = (ltot == 0.f) ? -INFINITY : (m2 + log2f(ltot)) * kLn2;
+    }
+    return;
+  }
   if (qrow < N) {
     const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
 #pragma unroll

@@ -122,11 +122,9 @@ void fwd16_kernel(FwdParams p) {
   const int g = lane >> 5;
   const int r = lane & 31;
 
-  int unit = blockIdx.x;
-  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
-  const int bh = unit / p.n_qtiles;
-  int qt = unit % p.n_qtiles;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;
+  const Unit wu = decode_unit(p, blockIdx.x);
+  const int bh = wu.bh;
+  const int qt = wu.qt;
   const int b = bh / (int)p.H;
   const int h = bh % (int)p.H;
   const int n = (int)p.N;
@@ -157,7 +155,11 @@ void fwd16_kernel(FwdParams p) {
     kv_hi = min(kv_hi, q0 + BR);
     wave_hi = min(wave_hi, qw + 32);
   }
-  const int ntiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
+  // Key tiles [t_lo, t_hi) of this unit's split (all of them without a split).
+  const int all_tiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
+  const int chunk = (all_tiles + p.n_splits - 1) / p.n_splits;
+  const int t_lo = min(all_tiles, wu.split * chunk);
+  const int t_hi = min(all_tiles, t_lo + chunk);
 
   // ---- per-lane constants of the global -> LDS copies: block blk = wave*LPW + i holds
   // rows blk*RPB .. +RPB-1; this lane fills the block's 16-byte slot `lane`, i.e. physical
@@ -233,12 +235,12 @@ void fwd16_kernel(FwdParams p) {
   float lsum = 0.f;        // this lane half's share of the denominator
   const float c = p.scale_log2;
 
-  // Tile t lives in buffer t & 1 and is copied one tile ahead.
-  if (ntiles > 0) issue_tile(0, 0);
+  // Tile t lives in buffer (t - t_lo) & 1 and is copied one tile ahead.
+  if (t_lo < t_hi) issue_tile(t_lo * BC, 0);
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int t = t_lo; t < t_hi; ++t) {
     const int j0 = t * BC;
-    const int buf = t & 1;
+    const int buf = (t - t_lo) & 1;
     const unsigned char* kb = lds + buf * 2 * TILEB;
     const unsigned char* vb = kb + TILEB;
     wait_vmem();  // this wave's copies of tile t have landed
@@ -254,7 +256,7 @@ void fwd16_kernel(FwdParams p) {
       }
     }
     __syncthreads();  // tile t visible to all waves; all waves are done with tile t-1
-    if (t + 1 < ntiles) issue_tile(j0 + BC, buf ^ 1);
+    if (t + 1 < t_hi) issue_tile(j0 + BC, buf ^ 1);
 
     if (j0 < wave_hi) {
       // ---- S^T = K . Q^T. The sub-tiles' products advance together, one reduction step
@@ -371,6 +373,27 @@ void fwd16_kernel(FwdParams p) {
 
   // ---- epilogue
   const float ltot = pair_sum(lsum);
+  if (p.n_splits > 1) {
+    // Normalised partial state of this split, in float32, for the merge kernel.
+    if (qrow < n) {
+      const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
+      const int64_t prow = ((int64_t)wu.split * p.BH + bh) * n + qrow;
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          float4 o4;
+          o4.x = oacc[dt][4 * a4 + 0] * inv;
+          o4.y = oacc[dt][4 * a4 + 1] * inv;
+          o4.z = oacc[dt][4 * a4 + 2] * inv;
+          o4.w = oacc[dt][4 * a4 + 3] * inv;
+          *reinterpret_cast<float4*>(po + 32 * dt + 8 * a4 + 4 * g) = o4;
+        }
+      if (g == 0) p.part_lse[prow] = (ltot == 0.f) ? -INFINITY : (mref + log2f(ltot)) * kLn2;
+    }
+    return;
+  }
   if (qrow < n) {
     const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
 #pragma unroll

@@ -96,6 +96,65 @@ int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* 
                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
                    float scale, int causal, const int32_t* kv_len, int dtype, void* stream);
 
+/*
+ * fa_fwd_split_workspace_bytes - device workspace that fa_fwd_split needs for these sizes
+ * and n_splits: S*B*H*N*D float32 of partial O, padded to 256 bytes, then S*B*H*N float32
+ * of partial LSE. Returns 0 when n_splits == 1 or any size is 0, and -1 for a negative size,
+ * n_splits outside [1, 256], or sizes whose byte count overflows. Pure host arithmetic.
+ */
+int64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int n_splits);
+
+/*
+ * fa_fwd_split - fa_fwd_strided with the key axis of every query tile cut into n_splits
+ * parts that separate workgroups process, followed by a merge of the partial states.
+ * Partial softmax states over disjoint key sets combine associatively, with the empty set
+ * (O = 0, LSE = -inf) as identity ("Paper: FlashAttention", Objectives, Math & data
+ * structures), so the result is the same attention up to rounding. It raises the number of
+ * workgroups when B*H*ceil(N/128) alone does not fill the GPU (short batches, few heads).
+ *
+ * A query tile that sees T key tiles gives part s the tiles [s*c, min(T, (s+1)*c)),
+ * c = ceil(T / n_splits); a part with no key writes the identity state. The partial O is
+ * kept in float32 and normalised per part; the merge (fa_merge_states) rounds O once.
+ *
+ * n_splits        : 1..256. 1 is exactly fa_fwd_strided (the workspace is then unused).
+ * workspace       : device pointer, 256-byte aligned, at least
+ *                   fa_fwd_split_workspace_bytes(B, H, N, D, n_splits) bytes, not overlapping
+ *                   Q, K, V, O or LSE. Its contents on entry do not matter; on return it holds
+ *                   the partial states (part_o then part_lse, as fa_merge_states takes them).
+ * workspace_bytes : its size in bytes.
+ * Other arguments as fa_fwd_strided. Two kernels are launched on `stream`, nothing is
+ * allocated. Errors: n_splits out of range or a workspace that is too small gives
+ * FA_ERR_ARG, a NULL workspace FA_ERR_NULL, a misaligned one FA_ERR_ALIGN; otherwise as
+ * fa_fwd_strided. Calls that share one workspace on different streams race.
+ */
+int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
+                 float scale, int causal, const int32_t* kv_len, int dtype, int n_splits,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_merge_states - merge S partial attention states per row ("Paper: FlashAttention",
+ * Objectives, Math & data structures: the associative merge of partial softmax states).
+ * For row (b, h, n), with m = max_s LSE_s and w_s = exp(LSE_s - m):
+ *     LSE = m + ln(sum_s w_s),   O = sum_s w_s O_s / sum_s w_s;
+ * states with LSE_s = -inf are the identity and are skipped; a row whose every state is the
+ * identity gets O = 0 and LSE = -inf.
+ *
+ * part_o   : device pointer, contiguous float32 [S][B][H][N][D], each O_s normalised over
+ *            its own key set (16-byte aligned). Read only.
+ * part_lse : device pointer, contiguous float32 [S][B][H][N], natural-log LSE_s. Read only.
+ * n_states : S, 1..256.
+ * O        : device pointer of `dtype`, strided as o_strides (3 int64 element strides
+ *            {b, h, n} on the host, or NULL for contiguous [B][H][N][D]); fully overwritten.
+ * LSE      : device pointer, contiguous float32 [B][H][N]; fully overwritten.
+ * D        : 32, 64, 128 or 256 for every dtype.
+ * One kernel on `stream`; nothing is allocated. Errors as fa_fwd_strided, FA_ERR_ARG for
+ * n_states out of range.
+ */
+int fa_merge_states(const float* part_o, const float* part_lse, int n_states,
+                    int64_t B, int64_t H, int64_t N, int64_t D, void* O,
+                    const int64_t* o_strides, float* LSE, int dtype, void* stream);
+
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -177,3 +177,94 @@ def test_non_overlap_rule():
         assert call_strided(CONTIG[:9] + o, O=0) == binding.FA_ERR_NULL
     for o in bad:
         assert call_strided(CONTIG[:9] + o) == binding.FA_ERR_ARG
+
+
+# ---- key-split forward and partial-state merge
+
+WS = 0x100000   # 256-byte aligned stand-in workspace address
+
+
+def ws_formula(B, H, N, D, S):
+    part_o = S * B * H * N * D * 4
+    return (part_o + 255) // 256 * 256 + S * B * H * N * 4
+
+
+@pytest.mark.parametrize("B,H,N,D,S", [(1, 1, 1, 32, 2), (2, 3, 100, 64, 3), (2, 32, 8192, 128, 8),
+                                      (1, 4, 77, 256, 256)])
+def test_split_workspace_bytes(B, H, N, D, S):
+    assert fa.fa_fwd_split_workspace_bytes(B, H, N, D, S) == ws_formula(B, H, N, D, S)
+
+
+def test_split_workspace_bytes_edges():
+    assert fa.fa_fwd_split_workspace_bytes(2, 3, 100, 64, 1) == 0
+    assert fa.fa_fwd_split_workspace_bytes(0, 3, 100, 64, 4) == 0
+    for S in (0, -1, 257):
+        assert fa.fa_fwd_split_workspace_bytes(1, 1, 8, 64, S) == -1
+    assert fa.fa_fwd_split_workspace_bytes(-1, 1, 8, 64, 2) == -1
+    assert fa.fa_fwd_split_workspace_bytes(1 << 30, 1 << 20, 1 << 10, 128, 2) == -1
+
+
+def call_split(n_splits=2, workspace=WS, workspace_bytes=None, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    if workspace_bytes is None:
+        workspace_bytes = max(0, ws_formula(a["B"], a["H"], a["N"], a["D"], n_splits))
+    return fa.fa_fwd_split(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["D"], None,
+                           a["scale"], a["causal"], a["kv_len"], a["dtype"], n_splits, workspace, workspace_bytes,
+                           a["stream"])
+
+
+@pytest.mark.parametrize("S", [0, -3, 257])
+def test_split_count_out_of_range(S):
+    assert call_split(n_splits=S) == binding.FA_ERR_ARG
+
+
+def test_split_workspace_checks():
+    assert call_split(workspace=0) == binding.FA_ERR_NULL
+    assert call_split(workspace=WS + 16) == binding.FA_ERR_ALIGN
+    need = ws_formula(1, 1, 8, 64, 2)
+    assert call_split(workspace_bytes=need - 1) == binding.FA_ERR_ARG
+
+
+def test_split_shares_forward_validation():
+    assert call_split(B=-1) == binding.FA_ERR_SHAPE
+    assert call_split(D=96) == binding.FA_ERR_UNSUPPORTED
+    assert call_split(scale=0.0) == binding.FA_ERR_ARG
+    assert call_split(Q=0) == binding.FA_ERR_NULL
+    assert call_split(O=A + 8) == binding.FA_ERR_ALIGN
+    assert call_split(O=GOOD["K"]) == binding.FA_ERR_ARG
+
+
+def test_split_empty_is_noop():
+    assert call_split(N=0, Q=0, K=0, V=0, O=0, LSE=0, workspace=0) == binding.FA_OK
+
+
+def call_merge(n_states=2, o_strides=None, **kw):
+    a = dict(part_o=WS, part_lse=WS + 0x1000, B=1, H=2, N=8, D=64, O=A + 0x300, LSE=A + 0x400,
+             dtype=fa.FA_BF16, stream=0)
+    a.update(kw)
+    return fa.fa_merge_states(a["part_o"], a["part_lse"], n_states, a["B"], a["H"], a["N"], a["D"], a["O"],
+                              o_strides, a["LSE"], a["dtype"], a["stream"])
+
+
+def test_merge_validation():
+    assert call_merge(B=-1) == binding.FA_ERR_SHAPE
+    assert call_merge(D=96) == binding.FA_ERR_UNSUPPORTED
+    assert call_merge(dtype=7) == binding.FA_ERR_UNSUPPORTED
+    for S in (0, 257):
+        assert call_merge(n_states=S) == binding.FA_ERR_ARG
+    assert call_merge(part_o=0) == binding.FA_ERR_NULL
+    assert call_merge(part_lse=0) == binding.FA_ERR_NULL
+    assert call_merge(O=0) == binding.FA_ERR_NULL
+    assert call_merge(LSE=0) == binding.FA_ERR_NULL
+    assert call_merge(part_o=WS + 4) == binding.FA_ERR_ALIGN
+    assert call_merge(O=A + 8) == binding.FA_ERR_ALIGN
+    assert call_merge(LSE=A + 2) == binding.FA_ERR_ALIGN
+    assert call_merge(o_strides=[2 * 8 * 64, 8 * 64, -64]) == binding.FA_ERR_ARG
+    assert call_merge(o_strides=[2 * 8 * 64, 8 * 64, 4]) == binding.FA_ERR_ALIGN
+    assert call_merge(o_strides=[2 * 8 * 64, 0, 64]) == binding.FA_ERR_ARG      # heads overlap
+    assert call_merge(o_strides=[2 * 8 * 64, 8 * 64, 64], O=0) == binding.FA_ERR_NULL
+
+
+def test_merge_empty_is_noop():
+    assert call_merge(N=0, part_o=0, part_lse=0, O=0, LSE=0) == binding.FA_OK
