@@ -76,7 +76,8 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   const void* fn;
   if constexpr (k16) {
     using S = Shape16<D>;
-    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE>);
+    fn = sp.n > 1 ? reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, true>)
+                  : reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, false>);
   } else {
     fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
   }

@@ -99,15 +99,18 @@ struct FwdParams {
 struct Unit {
   int bh, qt, split;
 };
+// SPLIT = false compiles the unsplit case (n_splits == 1) without the split arithmetic.
+template <bool SPLIT>
 __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   int unit = bid;
   if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
   Unit u;
-  const int per_head = p.n_qtiles * p.n_splits;
+  const int ns = SPLIT ? p.n_splits : 1;
+  const int per_head = p.n_qtiles * ns;
   u.bh = unit / per_head;
   const int rem = unit % per_head;
-  u.qt = rem / p.n_splits;
-  u.split = rem % p.n_splits;
+  u.qt = rem / ns;
+  u.split = rem % ns;
   if (p.causal) u.qt = p.n_qtiles - 1 - u.qt;
   return u;
 }
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int g = lane >> 5;       // lane half
   const int r = lane & 31;       // query column of this lane / A-operand row
 
-  const Unit wu = decode_unit(p, blockIdx.x);
+  const Unit wu = decode_unit<true>(p, blockIdx.x);
   const int64_t bh = wu.bh;
   const int qt = wu.qt;
   const int64_t b = bh / p.H;

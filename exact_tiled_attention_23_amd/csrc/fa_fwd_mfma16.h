@@ -95,7 +95,7 @@ template <int D> __device__ __forceinline__ int swz_v(int j) {
   else return 0;  // D = 32: four consecutive rows already sit in four different bank quarters
 }
 
-template <typename T, int D, int BC, int NW, int WPE>
+template <typename T, int D, int BC, int NW, int WPE, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
@@ -122,7 +122,7 @@ void fwd16_kernel(FwdParams p) {
   const int g = lane >> 5;
   const int r = lane & 31;
 
-  const Unit wu = decode_unit(p, blockIdx.x);
+  const Unit wu = decode_unit<SPLIT>(p, blockIdx.x);
   const int bh = wu.bh;
   const int qt = wu.qt;
   const int b = bh / (int)p.H;
@@ -157,7 +157,8 @@ void fwd16_kernel(FwdParams p) {
   }
   // Key tiles [t_lo, t_hi) of this unit's split (all of them without a split).
   const int all_tiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
-  const int chunk = (all_tiles + p.n_splits - 1) / p.n_splits;
+  const int ns = SPLIT ? p.n_splits : 1;
+  const int chunk = (all_tiles + ns - 1) / ns;
   const int t_lo = min(all_tiles, wu.split * chunk);
   const int t_hi = min(all_tiles, t_lo + chunk);
 
@@ -373,7 +374,7 @@ void fwd16_kernel(FwdParams p) {
 
   // ---- epilogue
   const float ltot = pair_sum(lsum);
-  if (p.n_splits > 1) {
+  if constexpr (SPLIT) {
     // Normalised partial state of this split, in float32, for the merge kernel.
     if (qrow < n) {
       const float inv = (ltot == 0.f) ? 0.f : 1.f / ltot;
