@@ -15,8 +15,8 @@ from .build import LIB
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
-EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_merge_states",
-            "fa_strerror", "fa_abi_version")
+EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_fwd_split_count",
+            "fa_merge_states", "fa_strerror", "fa_abi_version")
 MAX_SPLITS = 256
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
@@ -48,6 +48,9 @@ def load_library():
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_fwd_split_count.restype = ctypes.c_int
+        lib.fa_fwd_split_count.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
+                                                                  ctypes.POINTER(ctypes.c_int)]
         lib.fa_merge_states.restype = ctypes.c_int
         lib.fa_merge_states.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -92,6 +95,13 @@ def fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dt
                                        workspace, workspace_bytes, stream)
 
 
+def fa_fwd_split_count(B, H, N, D, causal, dtype):
+    """Raw C call: returns (rc, suggested n_splits) for the current HIP device."""
+    n = ctypes.c_int(0)
+    rc = load_library().fa_fwd_split_count(B, H, N, D, causal, dtype, ctypes.byref(n))
+    return rc, n.value
+
+
 def fa_merge_states(part_o, part_lse, n_states, B, H, N, D, O, o_strides, LSE, dtype, stream):
     """Raw C call of the partial-state merge; o_strides None (contiguous) or 3 ints (b, h, n)."""
     arr = _int64_array(o_strides, 3, "o_strides")
@@ -131,7 +141,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     a device int32 tensor is passed through and clamped to [0, N] by the kernel).
 
     n_splits > 1 cuts every query tile's keys into that many parts processed by separate
-    workgroups, then merges the partial states (fa_fwd_split). workspace: None (a uint8
+    workgroups, then merges the partial states (fa_fwd_split); "auto" takes the count
+    fa_fwd_split_count suggests for the current device. workspace: None (a uint8
     device tensor is allocated) or a device tensor of at least
     fa_fwd_split_workspace_bytes(B, H, N, D, n_splits) bytes, 256-byte aligned.
     """
@@ -176,6 +187,9 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, strides,
             float(scale), 1 if causal else 0, kv_ptr, _TORCH_DTYPE[q.dtype])
     with torch.cuda.device(dev):
+        if n_splits == "auto":
+            rc, n_splits = fa_fwd_split_count(B, H, N, D, 1 if causal else 0, _TORCH_DTYPE[q.dtype])
+            _check(rc)
         if n_splits == 1 and workspace is None:
             rc = fa_fwd_strided(*args, handle)
         else:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "fa.h"
@@ -135,6 +136,50 @@ int dispatch_merge(int64_t D, const float* part_o, const float* part_lse, int S,
 }
 
 constexpr int kMaxSplits = 256;
+constexpr int kAutoSplitCap = 16;     // suggested part counts stay at or below this
+constexpr int kMinTilesPerPart = 4;   // and give every part at least this many key tiles
+
+// Suggested part count: enough work units to fill every workgroup slot of the GPU once
+// (twice for causal, whose query tiles differ in length), without parts shorter than
+// kMinTilesPerPart key tiles.
+template <typename T, int D>
+int suggest_splits(int64_t B, int64_t H, int64_t N, int causal, int* n_splits) {
+  constexpr bool k16 = sizeof(T) == 2;
+  constexpr int NW = k16 ? Shape16<D>::NW : kWaves;
+  constexpr int BR = 32 * NW;
+  constexpr int BC = k16 ? Shape16<D>::BC : kBlockKV;
+  const void* fn;
+  if constexpr (k16) {
+    using S = Shape16<D>;
+    fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, true>);
+  } else {
+    fn = reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, kBlockKV, kWaves>);
+  }
+  int dev = 0, n_cu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FA_ERR_HIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, 0) != hipSuccess) return FA_ERR_HIP;
+  const int64_t units = B * H * ((N + BR - 1) / BR);
+  const int64_t target = (int64_t)n_cu * (per_cu > 0 ? per_cu : 1) * (causal ? 2 : 1);
+  int64_t s = (target + units - 1) / units;
+  const int64_t key_tiles = (N + BC - 1) / BC;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, key_tiles / kMinTilesPerPart));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, kAutoSplitCap));
+  *n_splits = (int)s;
+  return FA_OK;
+}
+
+template <typename T>
+int suggest_splits_d(int64_t D, int64_t B, int64_t H, int64_t N, int causal, int* n_splits) {
+  switch (D) {
+    case 32: return suggest_splits<T, 32>(B, H, N, causal, n_splits);
+    case 64: return suggest_splits<T, 64>(B, H, N, causal, n_splits);
+    case 128: return suggest_splits<T, 128>(B, H, N, causal, n_splits);
+    default:
+      if constexpr (sizeof(T) == 2) return suggest_splits<T, 256>(B, H, N, causal, n_splits);
+      return FA_ERR_UNSUPPORTED;
+  }
+}
 
 // Workspace of a split forward: S*B*H*N*D floats of partial O, then (256-byte aligned)
 // S*B*H*N floats of partial LSE.
@@ -301,6 +346,26 @@ extern "C" int fa_fwd_split(const void* Q, const void* K, const void* V, void* O
   rc = run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype, s, sp);
   if (rc != FA_OK) return rc;
   return run_merge(sp.part_o, sp.part_lse, n_splits, B, H, N, D, O, st.o, LSE, dtype, s);
+}
+
+extern "C" int fa_fwd_split_count(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                                  int* n_splits) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (!supported(dtype, D)) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!n_splits) return FA_ERR_NULL;
+  if (B == 0 || H == 0 || N == 0) {
+    *n_splits = 1;
+    return FA_OK;
+  }
+  const int64_t lim = INT64_MAX / 16;
+  if (B > lim / H || B * H > lim / N || N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+  switch (dtype) {
+    case FA_BF16: return suggest_splits_d<__bf16>(D, B, H, N, causal, n_splits);
+    case FA_F16: return suggest_splits_d<_Float16>(D, B, H, N, causal, n_splits);
+    default: return suggest_splits_d<float>(D, B, H, N, causal, n_splits);
+  }
 }
 
 extern "C" int fa_merge_states(const float* part_o, const float* part_lse, int n_states, int64_t B, int64_t H,

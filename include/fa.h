@@ -133,6 +133,19 @@ int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LS
                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_split_count - a suggested n_splits for fa_fwd_split on the current HIP device.
+ * Picks the smallest count whose work units (B*H*query tiles*parts) fill every workgroup
+ * slot of the device once (twice when causal, whose query tiles differ in length), capped at
+ * 16 and so that every part keeps at least 4 key tiles; 1 when B*H*query tiles alone already
+ * do. The slot count comes from the device's compute-unit count and the kernel's occupancy.
+ * Writes the count (>= 1) to *n_splits and returns FA_OK; errors as fa_fwd for bad sizes,
+ * dtype, D or causal, FA_ERR_NULL for a NULL n_splits, FA_ERR_HIP if the device query fails.
+ * If any of B, H, N is 0 it writes 1 without a HIP call.
+ */
+int fa_fwd_split_count(int64_t B, int64_t H, int64_t N, int64_t D, int causal, int dtype,
+                       int* n_splits);
+
+/*
  * fa_merge_states - merge S partial attention states per row ("Paper: FlashAttention",
  * Objectives, Math & data structures: the associative merge of partial softmax states).
  * For row (b, h, n), with m = max_s LSE_s and w_s = exp(LSE_s - m):

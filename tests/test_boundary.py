@@ -268,3 +268,12 @@ def test_merge_validation():
 
 def test_merge_empty_is_noop():
     assert call_merge(N=0, part_o=0, part_lse=0, O=0, LSE=0) == binding.FA_OK
+
+
+def test_split_count_validation_and_empty():
+    assert fa.fa_fwd_split_count(-1, 1, 8, 64, 1, fa.FA_BF16)[0] == binding.FA_ERR_SHAPE
+    assert fa.fa_fwd_split_count(1, 1, 8, 96, 1, fa.FA_BF16)[0] == binding.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_split_count(1, 1, 8, 256, 1, fa.FA_F32)[0] == binding.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_split_count(1, 1, 8, 64, 2, fa.FA_BF16)[0] == binding.FA_ERR_ARG
+    assert binding.load_library().fa_fwd_split_count(1, 1, 8, 64, 1, fa.FA_BF16, None) == binding.FA_ERR_NULL
+    assert fa.fa_fwd_split_count(0, 4, 8192, 128, 1, fa.FA_BF16) == (binding.FA_OK, 1)

@@ -132,6 +132,27 @@ def test_split_full_size_small_batch():
         assert (lse - l0).abs().max().item() <= 1e-4
 
 
+def test_split_count_suggestions():
+    """The suggested count: 1 when the query tiles already fill the device, more for a long
+    sequence with few heads, 1 for a short one, never above 16; "auto" runs and matches the oracle."""
+    rc, s = fa.fa_fwd_split_count(2, 32, 8192, 128, 0, fa.FA_BF16)
+    assert rc == 0 and s == 1
+    rc, s = fa.fa_fwd_split_count(1, 4, 8192, 128, 1, fa.FA_BF16)
+    assert rc == 0 and 2 <= s <= 16
+    rc, s = fa.fa_fwd_split_count(1, 1, 100, 64, 1, fa.FA_F32)
+    assert rc == 0 and s == 1
+    for D, dt in ((32, fa.FA_F32), (64, fa.FA_F16), (256, fa.FA_BF16)):
+        rc, s = fa.fa_fwd_split_count(1, 1, 1 << 20, D, 1, dt)
+        assert rc == 0 and 1 <= s <= 16
+    x = generate(1, 2, 3000, 128, "bf16", causal=True, seed=12)
+    q, k, v = (t.to(DEV) for t in (x.q, x.k, x.v))
+    say("split auto")
+    o, lse = fa.forward(q, k, v, causal=True, scale=x.scale, n_splits="auto")
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True)
+    compare(o, lse, ro, rl, "bf16", "split auto")
+
+
 # ---- the merge on its own, fed partial states computed by the oracle
 
 
