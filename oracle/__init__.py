@@ -23,14 +23,24 @@ tiled.tiled_attention
 merge.merge_states
     The associative merge of two partial softmax states, with its identity
     element ("Paper: FlashAttention", Objectives, Math & data structures).
+backward.attention_grad, backward.attention_grad_rows
+    Gradients dQ, dK, dV of exact attention by the chain rule through the
+    definition (the softmax Jacobian written out).
+backward.tiled_backward
+    The pages' recomputing backward from saved (O, LSE), block by block, with
+    Delta = rowsum(dO o O) ("Paper: FlashAttention", Objectives, Math & data
+    structures; "vectorized-flash-attention-kernel", Key design decision 4).
 
 Every function is pinned by tests that do not reuse its own arithmetic:
 50-digit brute force on tiny inputs, closed forms, invariants and
-mutation checks.
+mutation checks; the gradients by finite differences of the pinned forward,
+by float64 autograd of an independent formulation, and by invariants.
 """
 
 from .naive import attention, key_counts
 from .tiled import tiled_attention
 from .merge import merge_states
+from .backward import attention_grad, attention_grad_rows, tiled_backward
 
-__all__ = ["attention", "key_counts", "tiled_attention", "merge_states"]
+__all__ = ["attention", "key_counts", "tiled_attention", "merge_states", "attention_grad", "attention_grad_rows",
+           "tiled_backward"]
