@@ -16,7 +16,7 @@ from .build import LIB
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_fwd_split_count",
-            "fa_merge_states", "fa_strerror", "fa_abi_version")
+            "fa_merge_states", "fa_bwd_workspace_bytes", "fa_bwd", "fa_strerror", "fa_abi_version")
 MAX_SPLITS = 256
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
@@ -55,6 +55,12 @@ def load_library():
         lib.fa_merge_states.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_int64
+        lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 4
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -108,6 +114,18 @@ def fa_merge_states(part_o, part_lse, n_states, B, H, N, D, O, o_strides, LSE, d
     return load_library().fa_merge_states(part_o, part_lse, n_states, B, H, N, D, O, arr, LSE, dtype, stream)
 
 
+def fa_bwd_workspace_bytes(B, H, N, D):
+    """Workspace bytes fa_bwd needs (-1 for invalid sizes)."""
+    return load_library().fa_bwd_workspace_bytes(B, H, N, D)
+
+
+def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype, workspace, workspace_bytes,
+           stream):
+    """Raw C call of the backward; pointers are ints (0 for NULL)."""
+    return load_library().fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype,
+                                 workspace, workspace_bytes, stream)
+
+
 def fa_strerror(code):
     return load_library().fa_strerror(code).decode()
 
@@ -125,6 +143,21 @@ def _stream_handle(stream, dev):
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _kv_len_device(kv_len, B, N, dev):
+    if kv_len is None:
+        return None
+    if isinstance(kv_len, torch.Tensor) and kv_len.is_cuda:
+        if kv_len.dtype != torch.int32 or kv_len.shape != (B,) or not kv_len.is_contiguous():
+            raise ValueError("device kv_len must be a contiguous int32 tensor [B]")
+        return kv_len
+    kv_cpu = torch.as_tensor(kv_len).to(torch.int64).reshape(-1)
+    if kv_cpu.shape != (B,):
+        raise ValueError("kv_len must have one entry per batch")
+    if B and (int(kv_cpu.min()) < 0 or int(kv_cpu.max()) > N):
+        raise ValueError("kv_len values must lie in [0, N]")
+    return kv_cpu.to(torch.int32).to(dev)
 
 
 def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None, stream=None, n_splits=1,
@@ -167,21 +200,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
         raise ValueError("out must be shaped and typed like q, with a contiguous head dimension")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
-    kv_ptr = 0
-    kv_dev = None
-    if kv_len is not None:
-        if isinstance(kv_len, torch.Tensor) and kv_len.is_cuda:
-            if kv_len.dtype != torch.int32 or kv_len.shape != (B,) or not kv_len.is_contiguous():
-                raise ValueError("device kv_len must be a contiguous int32 tensor [B]")
-            kv_dev = kv_len
-        else:
-            kv_cpu = torch.as_tensor(kv_len).to(torch.int64).reshape(-1)
-            if kv_cpu.shape != (B,):
-                raise ValueError("kv_len must have one entry per batch")
-            if B and (int(kv_cpu.min()) < 0 or int(kv_cpu.max()) > N):
-                raise ValueError("kv_len values must lie in [0, N]")
-            kv_dev = kv_cpu.to(torch.int32).to(dev)
-        kv_ptr = kv_dev.data_ptr()
+    kv_dev = _kv_len_device(kv_len, B, N, dev)
+    kv_ptr = 0 if kv_dev is None else kv_dev.data_ptr()
     handle = _stream_handle(stream, dev)
     strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, strides,
@@ -233,3 +253,46 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
                              list(out.stride()[:3]), lse.data_ptr(), _TORCH_DTYPE[dtype], _stream_handle(stream, dev))
     _check(rc)
     return out, lse
+
+
+def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the attention forward, from its outputs o and lse and the output
+    gradient do. q, k, v, o, do, dq, dk, dv: contiguous device tensors [B, H, N, D] of one dtype
+    (bfloat16 or float16); lse: contiguous float32 [B, H, N]. causal, scale and kv_len must be the
+    forward's. workspace: None (allocated here) or a device tensor of at least
+    fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte aligned."""
+    ts = (q, k, v, o, do)
+    if q.dtype not in (torch.bfloat16, torch.float16) or any(t.dtype != q.dtype for t in ts):
+        raise TypeError("q, k, v, o, do must share one dtype among bfloat16, float16")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, do must be [B, H, N, D] of one shape")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts):
+        raise ValueError("q, k, v, o, do must be contiguous device tensors")
+    B, H, N, D = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("dq, dk, dv must be contiguous device tensors shaped and typed like q")
+    need = fa_bwd_workspace_bytes(B, H, N, D)
+    if need < 0:
+        raise ValueError("sizes too large")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    kv_dev = _kv_len_device(kv_len, B, N, dev)
+    with torch.cuda.device(dev):
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, float(scale), 1 if causal else 0,
+                    0 if kv_dev is None else kv_dev.data_ptr(), _TORCH_DTYPE[q.dtype], workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    _check(rc)
+    return dq, dk, dv

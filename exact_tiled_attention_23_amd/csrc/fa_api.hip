@@ -10,10 +10,11 @@
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_mfma16.h"
 #include "fa_merge.h"
+#include "fa_bwd.h"
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
 // bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
@@ -302,7 +303,113 @@ int run_merge(const float* part_o, const float* part_lse, int S, int64_t B, int6
   }
 }
 
+// ---- backward
+constexpr int kBwdWaves = 4;   // 128 query rows (dQ kernel) or 128 keys (dK/dV kernel) per workgroup
+constexpr int kBwdKeyTile = 64;
+
+bool bwd_supported(int dtype, int64_t D) {
+  return (dtype == FA_BF16 || dtype == FA_F16) && (D == 32 || D == 64 || D == 128);
+}
+
+int64_t bwd_stats_bytes(int64_t BH, int64_t N) {
+  return BH * ((N + fa::kStatRows - 1) / fa::kStatRows) * (2 * fa::kStatRows) * 4;
+}
+
+bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+template <typename T, int D>
+int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipStream_t stream) {
+  constexpr int R = 32 * kBwdWaves;
+  const int64_t tiles = (N + R - 1) / R;
+  const int64_t units = B * H * tiles;
+  if (tiles > INT32_MAX || units > INT32_MAX) return FA_ERR_SHAPE;
+  fa::BwdParams p = base;
+  p.n_tiles = (int)tiles;
+  p.n_units = units;
+  p.xcd_groups = (units % 8 == 0) ? 8 : 1;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>),
+                                 dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>),
+                      dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <typename T>
+int dispatch_bwd(int64_t D, const fa::BwdParams& p, int64_t B, int64_t H, int64_t N, hipStream_t s) {
+  switch (D) {
+    case 32: return launch_bwd<T, 32>(p, B, H, N, s);
+    case 64: return launch_bwd<T, 64>(p, B, H, N, s);
+    default: return launch_bwd<T, 128>(p, B, H, N, s);
+  }
+}
+
 }  // namespace
+
+extern "C" int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return -1;
+  if (B == 0 || H == 0 || N == 0) return 0;
+  const int64_t lim = INT64_MAX / 1024;
+  if (B > lim / H || B * H > lim / (N + fa::kStatRows)) return -1;
+  return bwd_stats_bytes(B * H, N);
+}
+
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                      void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
+                      int causal, const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (!bwd_supported(dtype, D)) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  const int64_t lim = INT64_MAX / 16;
+  if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
+  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+  const int64_t need = fa_bwd_workspace_bytes(B, H, N, D);
+  if (need < 0) return FA_ERR_SHAPE;
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_NULL;
+  for (const void* ptr : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if (misaligned(ptr, 16)) return FA_ERR_ALIGN;
+  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4)) || misaligned(workspace, 256)) return FA_ERR_ALIGN;
+  if (workspace_bytes < need) return FA_ERR_ARG;
+  // Outputs (and the workspace, which is written) must not overlap each other or any input.
+  const int64_t tb = B * H * N * D * 2;
+  const void* outs[4] = {dQ, dK, dV, workspace};
+  const int64_t out_b[4] = {tb, tb, tb, need};
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const int64_t in_b[6] = {tb, tb, tb, tb, tb, B * H * N * 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return FA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return FA_ERR_ARG;
+  }
+  fa::BwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = LSE;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.stats = static_cast<float*>(workspace);
+  p.kv_len = kv_len;
+  p.H = H;
+  p.N = N;
+  p.scale = scale;
+  p.scale_log2 = scale * fa::kLog2e;
+  p.causal = causal;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return dtype == FA_BF16 ? dispatch_bwd<__bf16>(D, p, B, H, N, s) : dispatch_bwd<_Float16>(D, p, B, H, N, s);
+}
 
 extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
                               int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,

@@ -1,0 +1,471 @@
+// Exact attention backward by recomputation, bf16/f16 kernels for gfx950.
+//
+// The backward rebuilds each block of P from the forward's saved row statistics instead of
+// storing P ("vectorized-flash-attention-kernel", Key design decision 4: the stored per-row
+// statistics let any (query block, key block) pair of S and P be rebuilt for dQ, dK, dV;
+// "Paper: FlashAttention", Objectives, Math & data structures: the backward by recomputation
+// and the identity rowsum(dP o P) = rowsum(dO o O)). With LSE the natural-log statistic and
+// Delta_i = rowsum(dO_i o O_i):
+//
+//   P_ij  = exp(scale <q_i, k_j> - LSE_i)        (0 for masked pairs and rows with no key)
+//   dV_j  = sum_i P_ij dO_i
+//   dS_ij = P_ij (<dO_i, v_j> - Delta_i)
+//   dQ_i  = scale sum_j dS_ij k_j
+//   dK_j  = scale sum_i dS_ij q_i
+//
+// Two kernels, each the only writer of its outputs (no atomics; the result is the same on
+// every run):
+//
+//  * bwd_dq_kernel: one workgroup per (batch, head, query tile), each wave 32 queries; it
+//    walks the key tiles like the forward. S^T = K.Q^T and dP^T = V.dO^T on the matrix
+//    cores give each lane one query and 16 keys of every 32-key sub-tile, so P and dS are
+//    formed per lane and feed dQ^T = K^T.dS^T straight from the accumulator registers, with
+//    K^T fragments from transpose reads (ds_read_b64_tr_b16). Its prologue also forms
+//    Delta = rowsum(dO o O) and stores, per 64-row block, the rows' exponent offsets
+//    (LSE log2 e, +inf for a row with no key or past N) next to their Delta values.
+//  * bwd_dkdv_kernel: one workgroup per (batch, head, key tile), each wave 32 keys held in
+//    registers; it walks the query tiles. S = Q.K^T and dP = dO.V^T give each lane one key
+//    and 16 queries of every 32-query sub-tile (Q and dO rows are read in a permuted order so
+//    that the accumulator is exactly the next product's operand), so P and dS feed
+//    dV^T = dO^T.P and dK^T = Q^T.dS directly.
+//
+// Tiles go HBM -> LDS with direct 16-byte copies, double-buffered. Every tile is read both
+// row-wise and by transpose reads, so one XOR swizzle of the 16-byte chunks serves both
+// without bank conflicts (swz_u below).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_fwd_kernel.h"
+#include "fa_fwd_mfma16.h"
+
+namespace fa {
+
+struct BwdParams {
+  const void* q;      // contiguous [B][H][N][D]
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;   // [B][H][N], natural log
+  void* dq;           // outputs, contiguous [B][H][N][D]
+  void* dk;
+  void* dv;
+  float* stats;       // [B*H][ceil(N/64)][128] floats: 64 exponent offsets, then 64 Delta values
+  const int32_t* kv_len;
+  int64_t H, N;
+  float scale;
+  float scale_log2;   // scale * log2(e)
+  int causal;
+  int n_tiles;        // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
+  int64_t n_units;    // B * H * n_tiles
+  int xcd_groups;     // 8 when n_units % 8 == 0, else 1
+};
+
+constexpr int kStatRows = 64;  // rows per block of the stats array
+
+// Chunk swizzle for tiles read both as row fragments (16 lanes on 16 rows of one chunk) and
+// by transpose reads (16 lanes on 4 consecutive rows x 2 chunks): the physical chunk is the
+// logical one XOR swz_u(row).
+template <int D> __device__ __forceinline__ int swz_u(int j) {
+  if constexpr (D >= 128) return 4 * (j & 3) + ((j >> 2) & 3);
+  else if constexpr (D == 64) return 2 * ((j >> 1) & 3) + ((j >> 3) & 1);
+  else return (j >> 2) & 3;
+}
+
+__device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh) {
+  int unit = bid;
+  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
+  *bh = unit / p.n_tiles;
+  return unit % p.n_tiles;
+}
+
+// Per-lane copy plan of a [rows][D] tile into LDS, 1 KB per copy instruction: copy i of this
+// wave fills rows (wave*LPW + i)*RPB + lane/CPR, physical chunk lane%CPR.
+template <int D, int ROWS, int NW>
+struct TilePlan {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILEB = ROWS * ROWB;
+  static constexpr int LPW = TILEB / 1024 / NW;
+  static constexpr int RPB = 1024 / ROWB;
+  static_assert(TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
+  int row[LPW];
+  unsigned off[LPW];  // byte offset of this lane's 16 bytes within the tile in global memory
+  __device__ __forceinline__ TilePlan(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int j = (wave * LPW + i) * RPB + lane / CPR;
+      row[i] = j;
+      off[i] = j * ROWB + ((lane % CPR) ^ swz_u<D>(j)) * 16;
+    }
+  }
+  // Copy rows [r0, r0 + ROWS) of the tensor at `src` (n rows) into `dst`; rows past n read
+  // row n-1 instead.
+  __device__ __forceinline__ void issue(const unsigned char* src, int r0, int n, unsigned dst, int wave) const {
+    const unsigned char* t = src + (int64_t)r0 * ROWB;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int over = r0 + row[i] - (n - 1);
+      const unsigned back = over > 0 ? (unsigned)over * ROWB : 0u;
+      lds_copy16(t, off[i] - back, dst + (wave * LPW + i) * 1024);
+    }
+  }
+  // Zero this lane's slots of rows at or past `lim` (tile-relative).
+  __device__ __forceinline__ void zero_from(unsigned char* dst, int lim, int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      if (row[i] >= lim) *reinterpret_cast<uint4*>(dst + (wave * LPW + i) * 1024 + lane * 16) = uint4{0, 0, 0, 0};
+  }
+};
+
+// Row fragment (A operand, 32 rows x 16 of the reduction) at LDS tile `t`: row 32u + a_row_key(r),
+// reduction chunk 2s + g.
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::frag row_frag(const unsigned char* t, int row, int chunk) {
+  return *reinterpret_cast<const typename Mma<T>::frag*>(t + row * (2 * D) + ((chunk ^ swz_u<D>(row)) * 16));
+}
+
+// Transpose fragment: A operand whose rows are the head dimension (32 of them, block dt) and
+// whose reduction runs over 16 tile rows starting at `row0` (natural order).
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::frag tr_frag(const unsigned char* t, int row0, int dt, int lane) {
+  const int g = lane >> 5, s16 = lane & 15, s4 = s16 >> 2, sm = s16 & 3, q2 = (lane >> 4) & 1;
+  const int c = 4 * dt + 2 * q2 + (sm >> 1);
+  const int ra = row0 + 8 * g + s4, rb = ra + 4;
+  const unsigned char* pa = t + ra * (2 * D) + ((c ^ swz_u<D>(ra)) * 16) + (sm & 1) * 8;
+  const unsigned char* pb = t + rb * (2 * D) + ((c ^ swz_u<D>(rb)) * 16) + (sm & 1) * 8;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pb));
+  return __builtin_bit_cast(typename Mma<T>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ (and Delta, exponent offsets): one workgroup per (b, h, query tile of 32*NW rows).
+template <typename T, int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  static_assert(sizeof(T) == 2, "16-bit element types only");
+  constexpr int BR = 32 * NW;
+  constexpr int NSUB = BC / 32;
+  constexpr int NDT = D / 32;
+  constexpr int NQF = D / 16;
+  using Plan = TilePlan<D, BC, NW>;
+  constexpr int TILEB = Plan::TILEB;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * TILEB];  // [buf][K|V][tile]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int r = lane & 31;
+
+  int bh;
+  int qt = decode_tile(p, blockIdx.x, &bh);
+  if (p.causal) qt = p.n_tiles - 1 - qt;  // longest query tiles first
+  const int n = (int)p.N;
+  const int64_t base = (int64_t)bh * n * D;
+  const T* Qh = reinterpret_cast<const T*>(p.q) + base;
+  const T* Oh = reinterpret_cast<const T*>(p.o) + base;
+  const T* dOh = reinterpret_cast<const T*>(p.dout) + base;
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + base);
+  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + base);
+  T* dQh = reinterpret_cast<T*>(p.dq) + base;
+
+  const int q0 = qt * BR;
+  const int qw = q0 + 32 * wave;
+  const int qrow = qw + r;
+  const int b = bh / (int)p.H;
+  int kvl = n;
+  if (p.kv_len) {
+    const int x = p.kv_len[b];
+    kvl = x < 0 ? 0 : (x > n ? n : x);
+  }
+  int kv_hi = kvl, wave_hi = kvl;
+  if (p.causal) {
+    kv_hi = min(kv_hi, q0 + BR);
+    wave_hi = min(wave_hi, qw + 32);
+  }
+  const int ntiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
+
+  // ---- Q^T and dO^T fragments (B operands), Delta = rowsum(dO o O), exponent offset.
+  frag qf[NQF], dof[NQF];
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < NQF; ++s) {
+    if (qrow < n) {
+      qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * D + 16 * s + 8 * g);
+      dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * D + 16 * s + 8 * g);
+      const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * D + 16 * s + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)dof[s][e], (float)of[e], dsum);
+    } else {
+      qf[s] = frag{};
+      dof[s] = frag{};
+    }
+  }
+  const float delta = pair_sum(dsum);
+  const float lse = qrow < n ? p.lse[(int64_t)bh * n + qrow] : -INFINITY;
+  // P = 2^(s*c - mo): +inf offset for a row with no valid key (its P is 0).
+  const float mo = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+  {
+    const int n64 = (n + kStatRows - 1) / kStatRows;
+    if (g == 0 && qrow < n64 * kStatRows) {
+      float* st = p.stats + ((int64_t)bh * n64 + qrow / kStatRows) * (2 * kStatRows) + qrow % kStatRows;
+      st[0] = mo;
+      st[kStatRows] = qrow < n ? delta : 0.f;
+    }
+  }
+
+  const Plan plan(wave, lane);
+  const int kr = a_row_key<8>(r);
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
+  const float c = p.scale_log2;
+
+  auto issue = [&](int t, int buf) {
+    const unsigned kl = lds_address(lds + buf * 2 * TILEB);
+    plan.issue(Kh, t * BC, n, kl, wave);
+    plan.issue(Vh, t * BC, n, kl + TILEB, wave);
+  };
+  if (ntiles > 0) issue(0, 0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BC;
+    const int buf = t & 1;
+    unsigned char* kb = lds + buf * 2 * TILEB;
+    unsigned char* vb = kb + TILEB;
+    wait_vmem();
+    if (j0 + BC > kvl) {
+      // Rows at or past kv_len may hold anything: zero them so 0 * garbage cannot reach dQ.
+      plan.zero_from(kb, kvl - j0, wave, lane);
+      plan.zero_from(vb, kvl - j0, wave, lane);
+    }
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+
+    if (j0 < wave_hi) {
+      const bool edge = j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw);
+      int lim = kvl - j0;
+      if (p.causal) lim = min(lim, qrow - j0 + 1);
+      lim -= 8 * g;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        // S^T and dP^T for 32 keys (rows of K and V in the permuted order a_row_key).
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          const frag ka = row_frag<T, D>(kb, 32 * u + kr, 2 * st + g);
+          const frag va = row_frag<T, D>(vb, 32 * u + kr, 2 * st + g);
+          s = M::run(ka, qf[st], s);
+          dp = M::run(va, dof[st], dp);
+        }
+        // P and dS; register i of half g holds key 32u + 16(i/8) + 8g + i%8.
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo));
+          if (edge && 32 * u + 16 * (i / 8) + (i % 8) >= lim) x = 0.f;
+          ds[i] = x * (dp[i] - delta);
+        }
+        frag dsf[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsf[h][e] = (T)ds[8 * h + e];
+        // dQ^T += K^T . dS^T
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::run(tr_frag<T, D>(kb, 32 * u + 16 * h, dt, lane), dsf[h], acc[dt]);
+      }
+    }
+  }
+
+  // ---- dQ = scale * acc; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.
+  if (qrow < n) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        T o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (T)(acc[dt][4 * a4 + e] * p.scale);
+        *reinterpret_cast<uint2*>(dQh + (int64_t)qrow * D + 32 * dt + 8 * a4 + 4 * g) = *reinterpret_cast<const uint2*>(o4);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV: one workgroup per (b, h, key tile of 32*NW keys); query tiles of BQ rows.
+template <typename T, int D, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  static_assert(sizeof(T) == 2, "16-bit element types only");
+  static_assert(BQ == kStatRows, "one stats block per query tile");
+  constexpr int BKV = 32 * NW;
+  constexpr int NSUB = BQ / 32;
+  constexpr int NDT = D / 32;
+  constexpr int NQF = D / 16;
+  using Plan = TilePlan<D, BQ, NW>;
+  constexpr int TILEB = Plan::TILEB;
+  constexpr int STATB = 1024;                 // one copy instruction: the 512-byte stats block, twice
+  constexpr int BUFB = 2 * TILEB + STATB;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * BUFB];  // [buf][Q|dO|stats]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int r = lane & 31;
+
+  int bh;
+  const int kt = decode_tile(p, blockIdx.x, &bh);  // causal: key tile 0 has the most work
+  const int n = (int)p.N;
+  const int64_t base = (int64_t)bh * n * D;
+  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + base);
+  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + base);
+  const T* Kh = reinterpret_cast<const T*>(p.k) + base;
+  const T* Vh = reinterpret_cast<const T*>(p.v) + base;
+  T* dKh = reinterpret_cast<T*>(p.dk) + base;
+  T* dVh = reinterpret_cast<T*>(p.dv) + base;
+  const int n64 = (n + kStatRows - 1) / kStatRows;
+  const unsigned char* Sh = reinterpret_cast<const unsigned char*>(p.stats + (int64_t)bh * n64 * (2 * kStatRows));
+
+  const int k0 = kt * BKV;
+  const int kw = k0 + 32 * wave;
+  const int key = kw + r;
+  const int b = bh / (int)p.H;
+  int kvl = n;
+  if (p.kv_len) {
+    const int x = p.kv_len[b];
+    kvl = x < 0 ? 0 : (x > n ? n : x);
+  }
+  // Query tiles that can see some key of this tile: all of them, or from the diagonal on.
+  const int nqt = k0 < kvl ? (n + BQ - 1) / BQ : 0;
+  const int t0 = p.causal ? k0 / BQ : 0;
+
+  // ---- K^T and V^T fragments (B operands) of this lane's key; zero past kv_len, where
+  // P is forced to 0 as well.
+  const bool key_dead = key >= kvl;
+  frag kf[NQF], vf[NQF];
+#pragma unroll
+  for (int s = 0; s < NQF; ++s) {
+    if (key < kvl) {
+      kf[s] = *reinterpret_cast<const frag*>(Kh + (int64_t)key * D + 16 * s + 8 * g);
+      vf[s] = *reinterpret_cast<const frag*>(Vh + (int64_t)key * D + 16 * s + 8 * g);
+    } else {
+      kf[s] = frag{};
+      vf[s] = frag{};
+    }
+  }
+
+  const Plan plan(wave, lane);
+  const int qr = a_row_key<8>(r);
+  f32x16 dka[NDT], dva[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    dka[t] = f32x16{};
+    dva[t] = f32x16{};
+  }
+  const float c = p.scale_log2;
+  // Stats copy: lanes 0-31 bring the 512-byte block of 64 offsets and 64 Delta values,
+  // lanes 32-63 the same bytes again (the copy instruction always moves 1 KB).
+  const unsigned stat_off = (unsigned)(lane & 31) * 16;
+
+  auto issue = [&](int t, int buf) {
+    const unsigned ql = lds_address(lds + buf * BUFB);
+    plan.issue(Qh, t * BQ, n, ql, wave);
+    plan.issue(dOh, t * BQ, n, ql + TILEB, wave);
+    if (wave == 0) lds_copy16(Sh + (int64_t)t * (2 * kStatRows) * 4, stat_off, ql + 2 * TILEB);
+  };
+  if (t0 < nqt) issue(t0, 0);
+
+  for (int t = t0; t < nqt; ++t) {
+    const int i0 = t * BQ;
+    const int buf = (t - t0) & 1;
+    const unsigned char* qb = lds + buf * BUFB;
+    const unsigned char* ob = qb + TILEB;
+    const float* sb = reinterpret_cast<const float*>(qb + 2 * TILEB);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < nqt) issue(t + 1, buf ^ 1);
+
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+      const int qs = i0 + 32 * u;
+      if (p.causal && qs + 31 < kw) continue;  // every query of this sub-tile precedes every key of the wave
+      // S and dP for 32 queries (rows of Q and dO in the permuted order a_row_key).
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NQF; ++st) {
+        const frag qa = row_frag<T, D>(qb, 32 * u + qr, 2 * st + g);
+        const frag oa = row_frag<T, D>(ob, 32 * u + qr, 2 * st + g);
+        s = M::run(qa, kf[st], s);
+        dp = M::run(oa, vf[st], dp);
+      }
+      // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key.
+      float mo[16], dl[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4* pm = reinterpret_cast<const float4*>(sb + 32 * u + 16 * h + 8 * g);
+        const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * u + 16 * h + 8 * g);
+        const float4 m0 = pm[0], m1 = pm[1], d0 = pd[0], d1 = pd[1];
+        mo[8 * h + 0] = m0.x; mo[8 * h + 1] = m0.y; mo[8 * h + 2] = m0.z; mo[8 * h + 3] = m0.w;
+        mo[8 * h + 4] = m1.x; mo[8 * h + 5] = m1.y; mo[8 * h + 6] = m1.z; mo[8 * h + 7] = m1.w;
+        dl[8 * h + 0] = d0.x; dl[8 * h + 1] = d0.y; dl[8 * h + 2] = d0.z; dl[8 * h + 3] = d0.w;
+        dl[8 * h + 4] = d1.x; dl[8 * h + 5] = d1.y; dl[8 * h + 6] = d1.z; dl[8 * h + 7] = d1.w;
+      }
+      const bool diag = p.causal && qs < kw + 31;
+      float pr[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
+        if (key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key)) x = 0.f;
+        pr[i] = x;
+        ds[i] = x * (dp[i] - dl[i]);
+      }
+      frag pf[2], dsf[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[h][e] = (T)pr[8 * h + e];
+          dsf[h][e] = (T)ds[8 * h + e];
+        }
+      // dV^T += dO^T . P and dK^T += Q^T . dS
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dva[dt] = M::run(tr_frag<T, D>(ob, 32 * u + 16 * h, dt, lane), pf[h], dva[dt]);
+          dka[dt] = M::run(tr_frag<T, D>(qb, 32 * u + 16 * h, dt, lane), dsf[h], dka[dt]);
+        }
+    }
+  }
+
+  // ---- dK = scale * dka, dV = dva; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.
+  // Keys past kv_len have zero P and dS, so they store exact zeros.
+  if (key < n) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        T k4[4], v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = (T)(dka[dt][4 * a4 + e] * p.scale);
+          v4[e] = (T)dva[dt][4 * a4 + e];
+        }
+        const int64_t off = (int64_t)key * D + 32 * dt + 8 * a4 + 4 * g;
+        *reinterpret_cast<uint2*>(dKh + off) = *reinterpret_cast<const uint2*>(k4);
+        *reinterpret_cast<uint2*>(dVh + off) = *reinterpret_cast<const uint2*>(v4);
+      }
+  }
+}
+
+}  // namespace fa

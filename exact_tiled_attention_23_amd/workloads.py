@@ -17,6 +17,10 @@ Recipe (every workload):
   * the float32 draws are cast to the working dtype on the CPU with torch
     (round to nearest even);
   * scale = 1/sqrt(D) rounded to float32; the same number goes to both sides.
+
+Output gradients for the backward (``generate_grad_output``): iid standard normal
+dO [B, H, N, D] from its own ``default_rng(seed)``, drawn in float32 and cast the
+same way.
 """
 
 from dataclasses import dataclass, field
@@ -107,6 +111,14 @@ def generate(B, H, N, D, dtype, *, causal, seed, padding=False, q_row_scale=Fals
 def generate_workload(w: Workload, *, seed=None):
     return generate(w.B, w.H, w.N, w.D, w.dtype, causal=w.causal, seed=w.seed if seed is None else seed,
                     padding=w.padding, q_row_scale=w.q_row_scale)
+
+
+def generate_grad_output(B, H, N, D, dtype, *, seed):
+    """A seeded output gradient dO [B, H, N, D] in the working dtype (CPU tensor)."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.standard_normal((B, H, N, D), dtype=np.float32)).to(DTYPES[dtype])
 
 
 def to_f64(t):

@@ -168,6 +168,49 @@ int fa_merge_states(const float* part_o, const float* part_lse, int n_states,
                     int64_t B, int64_t H, int64_t N, int64_t D, void* O,
                     const int64_t* o_strides, float* LSE, int dtype, void* stream);
 
+/*
+ * fa_bwd_workspace_bytes - device workspace fa_bwd needs: B*H*ceil(N/64)*128 float32 (per
+ * 64-row block of each (b, h): the rows' exponent offsets, then their Delta values). 0 when any
+ * size is 0, -1 for a negative size or a byte count that overflows. Pure host arithmetic.
+ */
+int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+
+/*
+ * fa_bwd - gradients of the forward above by recomputation, asynchronous on `stream`
+ * ("vectorized-flash-attention-kernel", Key design decision 4: the forward's per-row
+ * statistics let every block of S and P be rebuilt for dQ, dK, dV; "Paper: FlashAttention",
+ * Objectives, Math & data structures: the backward by recomputation and the identity
+ * rowsum(dP o P) = rowsum(dO o O)). For the loss gradient dO = dL/dO:
+ *
+ *     P_ij  = exp(scale <q_i, k_j> - LSE_i)   (0 for masked pairs; J_i as for fa_fwd)
+ *     Delta_i = sum_d dO_id O_id
+ *     dV_j  = sum_i P_ij dO_i
+ *     dS_ij = P_ij (<dO_i, v_j> - Delta_i)
+ *     dQ_i  = scale sum_j dS_ij k_j,     dK_j = scale sum_i dS_ij q_i
+ *
+ * Keys at or past kv_len[b] get dK = dV = 0; rows with no valid key get dQ = 0.
+ *
+ * Q, K, V, O, dO : device pointers, contiguous [B][H][N][D] of `dtype` (read only). O and LSE
+ *           are the outputs of fa_fwd (or fa_fwd_strided / fa_fwd_split) for the same Q, K, V,
+ *           scale, causal and kv_len.
+ * LSE     : device pointer, contiguous [B][H][N] float32 (read only).
+ * dQ, dK, dV : device pointers, contiguous [B][H][N][D] of `dtype` (fully overwritten); they may
+ *           not overlap each other, any input, or the workspace.
+ * D       : 32, 64 or 128. dtype: FA_BF16 or FA_F16 (FA_F32 gives FA_ERR_UNSUPPORTED).
+ * workspace, workspace_bytes : device memory of at least fa_bwd_workspace_bytes(B, H, N, D)
+ *           bytes, 256-byte aligned; its contents on entry do not matter.
+ * Arithmetic: the products run on the matrix cores with float32 accumulation; P and dS are
+ * rounded to `dtype` before the products that take them; dQ, dK, dV are rounded on store.
+ * Two kernels run on `stream` (the second reads what the first writes to the workspace);
+ * dQ and dK/dV each have a single writer, so results are identical run to run.
+ * Errors as fa_fwd; a workspace that is too small, or overlapping outputs, give FA_ERR_ARG.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+           const void* dO, void* dQ, void* dK, void* dV,
+           int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+           const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
+           void* stream);
+
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -277,3 +277,59 @@ def test_split_count_validation_and_empty():
     assert fa.fa_fwd_split_count(1, 1, 8, 64, 2, fa.FA_BF16)[0] == binding.FA_ERR_ARG
     assert binding.load_library().fa_fwd_split_count(1, 1, 8, 64, 1, fa.FA_BF16, None) == binding.FA_ERR_NULL
     assert fa.fa_fwd_split_count(0, 4, 8192, 128, 1, fa.FA_BF16) == (binding.FA_OK, 1)
+
+
+# ---- backward
+
+def bwd_ws(B, H, N):
+    return B * H * ((N + 63) // 64) * 128 * 4
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100, 64) == bwd_ws(2, 3, 100)
+    assert fa.fa_bwd_workspace_bytes(2, 32, 8192, 128) == bwd_ws(2, 32, 8192)
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(-1, 3, 100, 64) == -1
+    assert fa.fa_bwd_workspace_bytes(1 << 40, 1 << 20, 1 << 20, 64) == -1
+
+
+TB = 2 * 3 * 8 * 64 * 2          # bytes of one [2, 3, 8, 64] bf16 tensor
+BG = dict(Q=A, K=A + TB, V=A + 2 * TB, O=A + 3 * TB, LSE=A + 4 * TB, dO=A + 5 * TB, dQ=A + 6 * TB, dK=A + 7 * TB,
+          dV=A + 8 * TB, B=2, H=3, N=8, D=64, scale=0.125, causal=1, kv_len=0, dtype=fa.FA_BF16,
+          ws=A + 16 * TB, ws_bytes=bwd_ws(2, 3, 8), stream=0)
+
+
+def call_bwd(**kw):
+    a = dict(BG)
+    a.update(kw)
+    return fa.fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dO"], a["dQ"], a["dK"], a["dV"], a["B"], a["H"],
+                     a["N"], a["D"], a["scale"], a["causal"], a["kv_len"], a["dtype"], a["ws"], a["ws_bytes"],
+                     a["stream"])
+
+
+def test_bwd_validation():
+    assert call_bwd(B=-1) == binding.FA_ERR_SHAPE
+    assert call_bwd(dtype=fa.FA_F32) == binding.FA_ERR_UNSUPPORTED
+    assert call_bwd(dtype=9) == binding.FA_ERR_UNSUPPORTED
+    for D in (16, 96, 256):
+        assert call_bwd(D=D) == binding.FA_ERR_UNSUPPORTED
+    assert call_bwd(scale=float("nan")) == binding.FA_ERR_ARG
+    assert call_bwd(causal=3) == binding.FA_ERR_ARG
+    for f in ("Q", "K", "V", "O", "LSE", "dO", "dQ", "dK", "dV", "ws"):
+        assert call_bwd(**{f: 0}) == binding.FA_ERR_NULL, f
+    for f in ("Q", "K", "V", "O", "dO", "dQ", "dK", "dV"):
+        assert call_bwd(**{f: BG[f] + 8}) == binding.FA_ERR_ALIGN, f
+    assert call_bwd(LSE=BG["LSE"] + 2) == binding.FA_ERR_ALIGN
+    assert call_bwd(ws=BG["ws"] + 16) == binding.FA_ERR_ALIGN
+    assert call_bwd(ws_bytes=bwd_ws(2, 3, 8) - 1) == binding.FA_ERR_ARG
+
+
+def test_bwd_overlap_rejected():
+    assert call_bwd(dQ=BG["Q"]) == binding.FA_ERR_ARG          # output on an input
+    assert call_bwd(dK=BG["dQ"] + TB // 2) == binding.FA_ERR_ARG  # outputs overlap
+    assert call_bwd(dV=BG["LSE"]) == binding.FA_ERR_ARG          # output on LSE
+    assert call_bwd(ws=BG["dV"] - 256 + TB) == binding.FA_ERR_ARG  # workspace over an output
+
+
+def test_bwd_empty_is_noop():
+    assert call_bwd(N=0, Q=0, K=0, V=0, O=0, LSE=0, dO=0, dQ=0, dK=0, dV=0, ws=0) == binding.FA_OK
