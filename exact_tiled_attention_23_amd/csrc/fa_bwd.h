@@ -144,7 +144,7 @@ __device__ __forceinline__ typename Mma<T>::frag tr_frag(const unsigned char* t,
 // ------------------------------------------------------------------------------------------
 // dQ (and Delta, exponent offsets): one workgroup per (b, h, query tile of 32*NW rows).
 template <typename T, int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   static_assert(sizeof(T) == 2, "16-bit element types only");
@@ -301,8 +301,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------------------------------
 // dK, dV: one workgroup per (b, h, key tile of 32*NW keys); query tiles of BQ rows.
+// Two waves per SIMD where the registers allow it; at D = 128 the K, V fragments and the dK, dV
+// accumulators alone take 192 registers, so one.
+template <int D> constexpr int dkdv_waves_per_eu() { return D >= 128 ? 1 : 2; }
+
 template <typename T, int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D>(), dkdv_waves_per_eu<D>())))
+void bwd_dkdv_kernel(BwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   static_assert(sizeof(T) == 2, "16-bit element types only");
