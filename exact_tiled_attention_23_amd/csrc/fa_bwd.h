@@ -254,21 +254,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       lim -= 8 * g;
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        // S^T and dP^T for 32 keys (rows of K and V in the permuted order a_row_key).
+        // S^T and dP^T for 32 keys (rows of K and V in the permuted order a_row_key), with the
+        // row fragments of step st+PD and the K^T transpose fragments of the dQ product below
+        // read while step st's products run (order pinned as in the dK/dV kernel).
         f32x16 s = f32x16{}, dp = f32x16{};
+        // At D = 128 only the first half of the K^T fragments is read ahead (all of them would
+        // not fit in the registers of two waves per SIMD); the second half is read while the
+        // first half's products run.
+        constexpr int KTH = D >= 128 ? 1 : 2;
+        frag kt[2][NDT];
+        {
+          constexpr int PD = 2;
+          static_assert(2 * 2 * NDT == 2 * NQF, "transpose reads per step");
+          frag ka[PD + 1], va[PD + 1];
 #pragma unroll
-        for (int st = 0; st < NQF; ++st) {
-          const frag ka = row_frag<T, D>(kb, 32 * u + kr, 2 * st + g);
-          const frag va = row_frag<T, D>(vb, 32 * u + kr, 2 * st + g);
-          s = M::run(ka, qf[st], s);
-          dp = M::run(va, dof[st], dp);
+          for (int st = 0; st < PD; ++st) {
+            ka[st] = row_frag<T, D>(kb, 32 * u + kr, 2 * st + g);
+            va[st] = row_frag<T, D>(vb, 32 * u + kr, 2 * st + g);
+          }
+#pragma unroll
+          for (int st = 0; st < NQF; ++st) {
+            if (st + PD < NQF) {
+              ka[(st + PD) % (PD + 1)] = row_frag<T, D>(kb, 32 * u + kr, 2 * (st + PD) + g);
+              va[(st + PD) % (PD + 1)] = row_frag<T, D>(vb, 32 * u + kr, 2 * (st + PD) + g);
+            }
+            s = M::run(ka[st % (PD + 1)], qf[st], s);
+            dp = M::run(va[st % (PD + 1)], dof[st], dp);
+          }
+#pragma unroll
+          for (int h = 0; h < KTH; ++h)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) kt[h][dt] = tr_frag<T, D>(kb, 32 * u + 16 * h, dt, lane);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
+#pragma unroll
+          for (int st = 0; st < NQF; ++st) {
+            if (st + PD < NQF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // row reads of st+PD
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // products of st
+            __builtin_amdgcn_sched_group_barrier(0x100, KTH, 0);                  // transpose reads
+          }
         }
         // P and dS; register i of half g holds key 32u + 16(i/8) + 8g + i%8.
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo));
-          if (edge && 32 * u + 16 * (i / 8) + (i % 8) >= lim) x = 0.f;
+          x = (edge && 32 * u + 16 * (i / 8) + (i % 8) >= lim) ? 0.f : x;
           ds[i] = x * (dp[i] - delta);
         }
         frag dsf[2];
@@ -277,10 +307,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
           for (int e = 0; e < 8; ++e) dsf[h][e] = (T)ds[8 * h + e];
         // dQ^T += K^T . dS^T
+        if constexpr (KTH == 1) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) kt[1][dt] = tr_frag<T, D>(kb, 32 * u + 16, dt, lane);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::run(tr_frag<T, D>(kb, 32 * u + 16 * h, dt, lane), dsf[h], acc[dt]);
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::run(kt[h][dt], dsf[h], acc[dt]);
       }
     }
   }
@@ -405,14 +439,46 @@ void bwd_dkdv_kernel(BwdParams p) {
     for (int u = 0; u < NSUB; ++u) {
       const int qs = i0 + 32 * u;
       if (p.causal && qs + 31 < kw) continue;  // every query of this sub-tile precedes every key of the wave
-      // S and dP for 32 queries (rows of Q and dO in the permuted order a_row_key).
+      // S and dP for 32 queries (rows of Q and dO in the permuted order a_row_key). The row
+      // fragments of step st+PD are read while step st's products run, and the transpose
+      // fragments of the dV/dK products below are read in the same stretch, so no product
+      // waits on a read issued just before it. The order is pinned with scheduling-group
+      // barriers (the scheduler otherwise places each read right before its product).
       f32x16 s = f32x16{}, dp = f32x16{};
+      frag tq[2][NDT], to[2][NDT];
+      {
+        constexpr int PD = 2;
+        // 16 transpose fragments of two reads each: 4 reads per reduction step at every D.
+        static_assert(4 * 2 * NDT == 4 * NQF, "transpose reads per step");
+        frag qa[PD + 1], oa[PD + 1];
 #pragma unroll
-      for (int st = 0; st < NQF; ++st) {
-        const frag qa = row_frag<T, D>(qb, 32 * u + qr, 2 * st + g);
-        const frag oa = row_frag<T, D>(ob, 32 * u + qr, 2 * st + g);
-        s = M::run(qa, kf[st], s);
-        dp = M::run(oa, vf[st], dp);
+        for (int st = 0; st < PD; ++st) {
+          qa[st] = row_frag<T, D>(qb, 32 * u + qr, 2 * st + g);
+          oa[st] = row_frag<T, D>(ob, 32 * u + qr, 2 * st + g);
+        }
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          if (st + PD < NQF) {
+            qa[(st + PD) % (PD + 1)] = row_frag<T, D>(qb, 32 * u + qr, 2 * (st + PD) + g);
+            oa[(st + PD) % (PD + 1)] = row_frag<T, D>(ob, 32 * u + qr, 2 * (st + PD) + g);
+          }
+          s = M::run(qa[st % (PD + 1)], kf[st], s);
+          dp = M::run(oa[st % (PD + 1)], vf[st], dp);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            to[h][dt] = tr_frag<T, D>(ob, 32 * u + 16 * h, dt, lane);
+            tq[h][dt] = tr_frag<T, D>(qb, 32 * u + 16 * h, dt, lane);
+          }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
+#pragma unroll
+        for (int st = 0; st < NQF; ++st) {
+          if (st + PD < NQF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // row reads of st+PD
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // products of st
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                    // transpose reads
+        }
       }
       // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key.
       float mo[16], dl[16];
@@ -431,7 +497,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
-        if (key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key)) x = 0.f;
+        const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
+        x = dead ? 0.f : x;
         pr[i] = x;
         ds[i] = x * (dp[i] - dl[i]);
       }
@@ -448,8 +515,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          dva[dt] = M::run(tr_frag<T, D>(ob, 32 * u + 16 * h, dt, lane), pf[h], dva[dt]);
-          dka[dt] = M::run(tr_frag<T, D>(qb, 32 * u + 16 * h, dt, lane), dsf[h], dka[dt]);
+          dva[dt] = M::run(to[h][dt], pf[h], dva[dt]);
+          dka[dt] = M::run(tq[h][dt], dsf[h], dka[dt]);
         }
     }
   }
