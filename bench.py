@@ -6,12 +6,18 @@ launch of the fused kernel: Q.K^T, masks, online softmax, P.V, normalisation and
 LSE). Inputs and outputs are resident in device memory before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --backward [--workload NAME] ...   (the backward pass instead: fa_bwd)
 
 FLOPs are algorithmic: 4*D per unmasked (query, key) pair, so the causal
 triangle and padded keys are counted once and only where they are computed by
 the definition. The roofline figure divides those FLOPs by the kernel's own
 average duration, measured with events recorded on the launch stream around
 every timed launch.
+
+With --backward a step is one fa_bwd call (its two kernels) on the same workload,
+with O and LSE from one forward and a seeded dO. Its algorithmic FLOPs are the
+five products of 2*D per unmasked pair (S rebuilt, dP, dV, dK, dQ), 10*D per pair;
+the kernels execute seven (S and dP are formed in both), reported beside it.
 """
 
 import argparse
@@ -25,11 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s and % bf16 MFMA peak, B2 H32 N8192 D128 bf16"
+METRIC_BWD = "attn bwd TFLOP/s (5 products of 2D flops per pair) and % bf16 MFMA peak"
 # MI355X published dense matrix peaks, TFLOP/s, and HBM3E bandwidth, GB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_tiled_attention_23_amd/csrc/fa_fwd_kernel.h", "exact_tiled_attention_23_amd/csrc/fa_fwd_mfma16.h",
-                  "exact_tiled_attention_23_amd/csrc/fa_merge.h", "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
+                  "exact_tiled_attention_23_amd/csrc/fa_merge.h", "exact_tiled_attention_23_amd/csrc/fa_bwd.h",
+                  "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -111,6 +119,31 @@ def cpu_baseline(x, w, heads):
             "seconds": round(dt, 3)}
 
 
+def cpu_baseline_backward(x, do, w, heads):
+    """The float64 gradient oracle on the first `heads` (batch, head) pairs, all rows."""
+    import numpy as np
+    import oracle
+    from exact_tiled_attention_23_amd.workloads import to_f64
+    from threadpoolctl import threadpool_limits
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads = min(heads, w.B * w.H)
+    pairs = 0
+    i = np.arange(w.N, dtype=np.int64)
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        for j in range(heads):
+            b, h = divmod(j, w.H)
+            L = w.N if x.kv_len is None else int(x.kv_len[b])
+            pairs += int((np.minimum(L, i + 1) if w.causal else np.full(w.N, L)).sum())
+            oracle.attention_grad(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
+                                  to_f64(x.v[b:b + 1, h:h + 1]), to_f64(do[b:b + 1, h:h + 1]), x.scale,
+                                  causal=w.causal, kv_len=None if x.kv_len is None else x.kv_len[b:b + 1])
+    dt = time.perf_counter() - t0
+    return {"value": 10.0 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} query rows, float64",
+            "seconds": round(dt, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +153,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="(batch, head) pairs the CPU oracle baseline runs; all of the headline workload by default")
+    ap.add_argument("--backward", action="store_true", help="time the backward (fa_bwd) instead of the forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes per step "
                          "(scale reference for the HBM byte counters)")
@@ -136,7 +170,7 @@ def main():
     import numpy as np
     import torch
     import exact_tiled_attention_23_amd as fa
-    from exact_tiled_attention_23_amd.workloads import HEADLINE, WORKLOADS, generate_workload
+    from exact_tiled_attention_23_amd.workloads import HEADLINE, WORKLOADS, generate_grad_output, generate_workload
 
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
@@ -158,9 +192,22 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    def step():
+    if args.backward:
+        if w.dtype == "f32":
+            print("the backward is built for bf16 and f16", file=sys.stderr)
+            sys.exit(2)
+        do_cpu = generate_grad_output(w.B, w.H, w.N, w.D, w.dtype, seed=w.seed + 1000)
+        do = do_cpu.to(dev)
         fa.forward(q, k, v, causal=w.causal, scale=x.scale, kv_len=kv, out=o, lse=lse, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=x.scale, kv_len=kv, dq=dq, dk=dk, dv=dv,
+                        workspace=ws, stream=stream)
+    else:
+        def step():
+            fa.forward(q, k, v, causal=w.causal, scale=x.scale, kv_len=kv, out=o, lse=lse, stream=stream)
 
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -181,23 +228,35 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     pairs = pair_count(w, x.kv_len)
-    flops = 4.0 * w.D * pairs
+    flops = (10.0 if args.backward else 4.0) * w.D * pairs
     elt = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     nbytes = algorithmic_bytes(w, x.kv_len, elt)
+    if args.backward:
+        # Q, K, V, O, dO read and dQ, dK, dV written once; LSE read once.
+        nbytes = 8 * elt * w.B * w.H * w.N * w.D + 4 * w.B * w.H * w.N
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+                "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(("bwd:" if args.backward else "") + name),
                 "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
                 "hbm_gbs_algorithmic": round(nbytes / avg_kernel_s / 1e9, 1),
                 "kernel_ms_avg": round(avg_kernel_s * 1e3, 4), "kernel_ms_min": round(min(kernel_ms), 4),
                 "kernel_ms_median": round(float(np.median(kernel_ms)), 4)}
+    if args.backward:
+        roofline["executed_flops"] = 14.0 * w.D * pairs
+        roofline["executed_tflops"] = round(14.0 * w.D * pairs / avg_kernel_s / 1e12, 2)
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"bench: CPU oracle baseline on {args.cpu_heads} heads")
-        cpu = cpu_baseline(x, w, args.cpu_heads)
-    line = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        if args.backward:
+            heads = min(args.cpu_heads, 2)
+            log(f"bench: CPU gradient oracle baseline on {heads} heads")
+            cpu = cpu_baseline_backward(x, do_cpu, w, heads)
+        else:
+            log(f"bench: CPU oracle baseline on {args.cpu_heads} heads")
+            cpu = cpu_baseline(x, w, args.cpu_heads)
+    line = {"metric": METRIC_BWD if args.backward else METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
             "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "D": w.D, "causal": w.causal,
