@@ -154,6 +154,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="(batch, head) pairs the CPU oracle baseline runs; all of the headline workload by default")
     ap.add_argument("--backward", action="store_true", help="time the backward (fa_bwd) instead of the forward")
+    ap.add_argument("--shape", default=None,
+                    help="B,H,N,D,dtype,causal: a seeded synthetic workload of this shape instead of a named one "
+                         "(the recipe of the named workloads, seed 7)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes per step "
                          "(scale reference for the HBM byte counters)")
@@ -170,7 +173,8 @@ def main():
     import numpy as np
     import torch
     import exact_tiled_attention_23_amd as fa
-    from exact_tiled_attention_23_amd.workloads import HEADLINE, WORKLOADS, generate_grad_output, generate_workload
+    from exact_tiled_attention_23_amd.workloads import (HEADLINE, WORKLOADS, Workload, generate_grad_output,
+                                                        generate_workload)
 
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
@@ -182,8 +186,14 @@ def main():
                           "bytes_written_per_step": src.numel() * 4, "steps": args.warmup + args.steps}))
         return
 
-    name = args.workload or HEADLINE
-    w = WORKLOADS[name]
+    if args.shape:
+        B, H, N, D, dt, causal = args.shape.split(",")
+        causal = causal.strip().lower() in ("1", "true", "causal")
+        name = f"b{B}h{H}n{N}d{D}-{dt}" + ("-causal" if causal else "")
+        w = Workload(name, int(B), int(H), int(N), int(D), dt, causal, seed=7)
+    else:
+        name = args.workload or HEADLINE
+        w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     log(f"bench: generating {name}")
     x = generate_workload(w)
