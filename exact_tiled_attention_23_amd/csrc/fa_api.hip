@@ -334,8 +334,14 @@ int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipSt
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>),
                                  dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>),
-                      dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
+  if constexpr (D == 128) {
+    // K/V in LDS, eight waves (two per key group): two waves per SIMD at this head dimension.
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>),
+                        dim3((unsigned)units), dim3(64 * 8), args, 0, stream);
+  } else {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>),
+                        dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
+  }
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

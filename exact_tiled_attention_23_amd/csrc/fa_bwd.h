@@ -541,4 +541,213 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// dK, dV at D = 128 with two waves per SIMD: the registers cannot hold each wave's K and V
+// fragments next to its dK and dV accumulators (192 registers), so the workgroup's 128 keys of K
+// and V live in LDS (64 KB, loaded once) and are read as B operands at each use. Eight waves: a
+// pair of waves shares each 32-key group, and wave w takes the 32-query half w / 4 of every
+// 64-row query tile; at the end the pair's partial dK and dV are added through LDS.
+template <typename T, int D, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_lds_kernel(BwdParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  static_assert(sizeof(T) == 2, "16-bit element types only");
+  static_assert(BQ == kStatRows && BQ == 64, "one stats block per query tile, two halves of 32");
+  static_assert(NW == 8, "four key groups x two query halves");
+  constexpr int BKV = 128;
+  constexpr int NDT = D / 32;
+  constexpr int NQF = D / 16;
+  constexpr int PD = 1;  // fragments read one reduction step ahead (two would spill)
+  using KPlan = TilePlan<D, BKV, NW>;
+  using QPlan = TilePlan<D, BQ, NW>;
+  constexpr int KTB = KPlan::TILEB;            // K (or V) tile bytes
+  constexpr int QTB = QPlan::TILEB;            // Q (or dO) tile bytes
+  constexpr int STATB = 1024;
+  constexpr int BUFB = 2 * QTB + STATB;
+  constexpr int LDSB = 2 * KTB + 2 * BUFB;
+  static_assert(4 * 64 * 2 * NDT * 16 * 4 <= LDSB, "the partner partials fit in LDS");
+  static_assert(4 * 2 * NDT == 4 * NQF, "transpose reads per step");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDSB];  // [K|V][buf][Q|dO|stats]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int r = lane & 31;
+  const int kg = wave & 3;   // key group
+  const int qh = wave >> 2;  // query half of each tile
+
+  int bh;
+  const int kt = decode_tile(p, blockIdx.x, &bh);
+  const int n = (int)p.N;
+  const int64_t base = (int64_t)bh * n * D;
+  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + base);
+  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + base);
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + base);
+  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + base);
+  T* dKh = reinterpret_cast<T*>(p.dk) + base;
+  T* dVh = reinterpret_cast<T*>(p.dv) + base;
+  const int n64 = (n + kStatRows - 1) / kStatRows;
+  const unsigned char* Sh = reinterpret_cast<const unsigned char*>(p.stats + (int64_t)bh * n64 * (2 * kStatRows));
+
+  const int k0 = kt * BKV;
+  const int kw = k0 + 32 * kg;
+  const int key = kw + r;
+  const int b = bh / (int)p.H;
+  int kvl = n;
+  if (p.kv_len) {
+    const int x = p.kv_len[b];
+    kvl = x < 0 ? 0 : (x > n ? n : x);
+  }
+  const int nqt = k0 < kvl ? (n + BQ - 1) / BQ : 0;
+  const int t0 = p.causal ? k0 / BQ : 0;
+  const bool key_dead = key >= kvl;
+
+  unsigned char* kb = lds;
+  unsigned char* vb = lds + KTB;
+  unsigned char* qbuf = lds + 2 * KTB;
+  const KPlan kplan(wave, lane);
+  const QPlan qplan(wave, lane);
+  const unsigned stat_off = (unsigned)(lane & 31) * 16;
+  auto issue = [&](int t, int buf) {
+    const unsigned ql = lds_address(qbuf + buf * BUFB);
+    qplan.issue(Qh, t * BQ, n, ql, wave);
+    qplan.issue(dOh, t * BQ, n, ql + QTB, wave);
+    if (wave == 0) lds_copy16(Sh + (int64_t)t * (2 * kStatRows) * 4, stat_off, ql + 2 * QTB);
+  };
+  if (t0 < nqt) {
+    kplan.issue(Kh, k0, n, lds_address(kb), wave);
+    kplan.issue(Vh, k0, n, lds_address(vb), wave);
+    issue(t0, 0);
+    wait_vmem();
+    // Keys at or past kv_len may hold anything: zero them so 0 * garbage cannot reach dK, dV.
+    if (k0 + BKV > kvl) {
+      kplan.zero_from(kb, kvl - k0, wave, lane);
+      kplan.zero_from(vb, kvl - k0, wave, lane);
+    }
+  }
+
+  const int qr = a_row_key<8>(r);
+  f32x16 dka[NDT], dva[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    dka[t] = f32x16{};
+    dva[t] = f32x16{};
+  }
+  const float c = p.scale_log2;
+
+  for (int t = t0; t < nqt; ++t) {
+    const int i0 = t * BQ;
+    const int buf = (t - t0) & 1;
+    const unsigned char* qb = qbuf + buf * BUFB;
+    const unsigned char* ob = qb + QTB;
+    const float* sb = reinterpret_cast<const float*>(qb + 2 * QTB);
+    if (t > t0) wait_vmem();
+    __syncthreads();
+    if (t + 1 < nqt) issue(t + 1, buf ^ 1);
+
+    const int qs = i0 + 32 * qh;
+    if (p.causal && qs + 31 < kw) continue;  // every query of this half precedes every key of the group
+    // S = Q K^T and dP = dO V^T for this wave's 32 queries (rows in the permuted order a_row_key)
+    // and 32 keys (B operands read from the K and V tiles), each step's fragments read PD steps
+    // ahead of its products.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    {
+      frag qa[PD + 1], oa[PD + 1], ka[PD + 1], va[PD + 1];
+      auto rd = [&](int st, int slot) {
+        qa[slot] = row_frag<T, D>(qb, 32 * qh + qr, 2 * st + g);
+        oa[slot] = row_frag<T, D>(ob, 32 * qh + qr, 2 * st + g);
+        ka[slot] = row_frag<T, D>(kb, 32 * kg + r, 2 * st + g);
+        va[slot] = row_frag<T, D>(vb, 32 * kg + r, 2 * st + g);
+      };
+#pragma unroll
+      for (int st = 0; st < PD; ++st) rd(st, st);
+#pragma unroll
+      for (int st = 0; st < NQF; ++st) {
+        if (st + PD < NQF) rd(st + PD, (st + PD) % (PD + 1));
+        s = M::run(qa[st % (PD + 1)], ka[st % (PD + 1)], s);
+        dp = M::run(oa[st % (PD + 1)], va[st % (PD + 1)], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * PD, 0);
+#pragma unroll
+      for (int st = 0; st < NQF; ++st) {
+        if (st + PD < NQF) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // fragments of st+PD
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // products of st
+      }
+    }
+    // Transpose fragments of the dV/dK products come two at a time (pair j = h*NDT + dt: dO^T and
+    // Q^T for 16 queries and 32 dims); pair 0 is read here, under the arithmetic below.
+    constexpr int NPAIR = 2 * NDT;
+    frag tto[2], ttq[2];
+    ttq[0] = tr_frag<T, D>(qb, 32 * qh, 0, lane);
+    tto[0] = tr_frag<T, D>(ob, 32 * qh, 0, lane);
+    // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key.
+    float mo[16], dl[16];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4* pm = reinterpret_cast<const float4*>(sb + 32 * qh + 16 * h + 8 * g);
+      const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * qh + 16 * h + 8 * g);
+      const float4 m0 = pm[0], m1 = pm[1], d0 = pd[0], d1 = pd[1];
+      mo[8 * h + 0] = m0.x; mo[8 * h + 1] = m0.y; mo[8 * h + 2] = m0.z; mo[8 * h + 3] = m0.w;
+      mo[8 * h + 4] = m1.x; mo[8 * h + 5] = m1.y; mo[8 * h + 6] = m1.z; mo[8 * h + 7] = m1.w;
+      dl[8 * h + 0] = d0.x; dl[8 * h + 1] = d0.y; dl[8 * h + 2] = d0.z; dl[8 * h + 3] = d0.w;
+      dl[8 * h + 4] = d1.x; dl[8 * h + 5] = d1.y; dl[8 * h + 6] = d1.z; dl[8 * h + 7] = d1.w;
+    }
+    const bool diag = p.causal && qs < kw + 31;
+    frag pf[2], dsf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
+      const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
+      x = dead ? 0.f : x;
+      pf[i / 8][i % 8] = (T)x;
+      dsf[i / 8][i % 8] = (T)(x * (dp[i] - dl[i]));
+    }
+    // dV^T += dO^T . P and dK^T += Q^T . dS, reading pair j+1 while pair j's products run.
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) {
+      if (j + 1 < NPAIR) {
+        ttq[(j + 1) & 1] = tr_frag<T, D>(qb, 32 * qh + 16 * ((j + 1) / NDT), (j + 1) % NDT, lane);
+        tto[(j + 1) & 1] = tr_frag<T, D>(ob, 32 * qh + 16 * ((j + 1) / NDT), (j + 1) % NDT, lane);
+      }
+      dva[j % NDT] = M::run(tto[j & 1], pf[j / NDT], dva[j % NDT]);
+      dka[j % NDT] = M::run(ttq[j & 1], dsf[j / NDT], dka[j % NDT]);
+    }
+  }
+
+  // ---- add the pair's partials: waves of the second query half hand theirs over through LDS.
+  __syncthreads();  // every wave is done with the tiles
+  float4* part = reinterpret_cast<float4*>(lds) + (kg * 2 * NDT * 4) * 64 + lane;
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        part[((2 * dt) * 4 + a4) * 64] = make_float4(dka[dt][4 * a4], dka[dt][4 * a4 + 1], dka[dt][4 * a4 + 2], dka[dt][4 * a4 + 3]);
+        part[((2 * dt + 1) * 4 + a4) * 64] = make_float4(dva[dt][4 * a4], dva[dt][4 * a4 + 1], dva[dt][4 * a4 + 2], dva[dt][4 * a4 + 3]);
+      }
+  }
+  __syncthreads();
+  if (qh == 1 || key >= n) return;
+  // dK = scale * dka, dV = dva; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 pk = part[((2 * dt) * 4 + a4) * 64];
+      const float4 pv = part[((2 * dt + 1) * 4 + a4) * 64];
+      const float ks[4] = {pk.x, pk.y, pk.z, pk.w}, vs[4] = {pv.x, pv.y, pv.z, pv.w};
+      T k4[4], v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k4[e] = (T)((dka[dt][4 * a4 + e] + ks[e]) * p.scale);
+        v4[e] = (T)(dva[dt][4 * a4 + e] + vs[e]);
+      }
+      const int64_t off = (int64_t)key * D + 32 * dt + 8 * a4 + 4 * g;
+      *reinterpret_cast<uint2*>(dKh + off) = *reinterpret_cast<const uint2*>(k4);
+      *reinterpret_cast<uint2*>(dVh + off) = *reinterpret_cast<const uint2*>(v4);
+    }
+}
+
 }  // namespace fa
