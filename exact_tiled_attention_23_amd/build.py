@@ -48,5 +48,26 @@ def build(verbose=False, extra_flags=()):
     return LIB
 
 
+CHECK_SRC = os.path.join(ROOT, "tests", "c", "fa_abi_check.cpp")
+CHECK_BIN = os.path.join(ROOT, "tests", "c", "fa_abi_check")
+
+
+def build_abi_check(verbose=False):
+    """Compile the C ABI check program (host code linking libfa.so through include/fa.h)."""
+    tmp = CHECK_BIN + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "-O2", "-std=c++17", f"-I{INCLUDE}", CHECK_SRC, "-o", tmp, f"-L{PKG}", "-lfa",
+           "-Wl,-rpath,$ORIGIN/../../exact_tiled_attention_23_amd"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, CHECK_BIN)
+    return CHECK_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_abi_check(verbose=True))
