@@ -1,0 +1,72 @@
+"""Seeded random shapes: forward, key-split forward and backward against the oracles.
+
+Thirty configurations drawn once from a fixed seed cover combinations that the hand-picked
+cases do not name: B, H, ragged N up to 700, every head dimension, both 16-bit types (and
+float32 for the forward), causal or not, key padding with random kv_len (0 included), and a
+random part count for the split. Tolerances are the ones of the dedicated tests.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_23_amd as fa
+from exact_tiled_attention_23_amd.workloads import generate, generate_grad_output, to_f64
+
+from test_backward_gpu import DTYPE_NAME, compare_grad, rounding_bound
+from test_parity_gpu import compare, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def draw_configs(count=30, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+        D = int(rng.choice([32, 64, 128] + ([] if dtype == "f32" else [256])))
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 701))
+        causal = bool(rng.integers(0, 2))
+        kv = None
+        if rng.random() < 0.5:
+            kv = rng.integers(0, N + 1, size=B).astype(np.int32)
+        splits = int(rng.integers(2, 9))
+        out.append((i, B, H, N, D, dtype, causal, kv, splits))
+    return out
+
+
+CONFIGS = draw_configs()
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"c{c[0]}")
+def test_random_shape(cfg):
+    i, B, H, N, D, dtype, causal, kv, splits = cfg
+    say(f"random c{i}: B={B} H={H} N={N} D={D} {dtype} causal={causal} kv_len={None if kv is None else kv.tolist()} "
+        f"splits={splits}")
+    x = generate(B, H, N, D, dtype, causal=causal, seed=5000 + i)
+    q, k, v = (t.to(DEV) for t in (x.q, x.k, x.v))
+    kl = None if kv is None else torch.as_tensor(kv)
+    q64, k64, v64 = to_f64(x.q), to_f64(x.k), to_f64(x.v)
+    ro, rl = oracle.attention(q64, k64, v64, x.scale, causal=causal, kv_len=kv)
+
+    o, lse = fa.forward(q, k, v, causal=causal, scale=x.scale, kv_len=kl)
+    torch.cuda.synchronize()
+    compare(o, lse, ro, rl, dtype, f"c{i} forward")
+
+    o2, lse2 = fa.forward(q, k, v, causal=causal, scale=x.scale, kv_len=kl, n_splits=splits)
+    torch.cuda.synchronize()
+    compare(o2, lse2, ro, rl, dtype, f"c{i} split {splits}")
+
+    if dtype != "f32" and D <= 128:
+        do = generate_grad_output(B, H, N, D, dtype, seed=6000 + i)
+        grads = fa.backward(q, k, v, o, lse, do.to(DEV), causal=causal, scale=x.scale, kv_len=kl)
+        torch.cuda.synchronize()
+        args = (q64, k64, v64, to_f64(do), x.scale)
+        ref = oracle.attention_grad(*args, causal=causal, kv_len=kv)
+        T = rounding_bound(*args, causal, kv, DTYPE_NAME[x.q.dtype])
+        for g, r, t, name in zip(grads, ref, T, ("dQ", "dK", "dV")):
+            compare_grad(g, r, t, dtype, f"c{i} {name}")
