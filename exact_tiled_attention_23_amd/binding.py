@@ -16,7 +16,7 @@ from .build import LIB
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_fwd_split_count",
-            "fa_merge_states", "fa_bwd_workspace_bytes", "fa_bwd", "fa_strerror", "fa_abi_version")
+            "fa_merge_states", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_strerror", "fa_abi_version")
 MAX_SPLITS = 256
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
@@ -61,6 +61,10 @@ def load_library():
         lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p]
+        lib.fa_bwd_strided.restype = ctypes.c_int
+        lib.fa_bwd_strided.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
+            ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -124,6 +128,14 @@ def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, d
     """Raw C call of the backward; pointers are ints (0 for NULL)."""
     return load_library().fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype,
                                  workspace, workspace_bytes, stream)
+
+
+def fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, strides, scale, causal, kv_len, dtype, workspace,
+                   workspace_bytes, stream):
+    """Raw C call of the strided backward; strides None (contiguous) or 24 ints."""
+    arr = _int64_array(strides, 24, "strides")
+    return load_library().fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, arr, scale, causal, kv_len,
+                                         dtype, workspace, workspace_bytes, stream)
 
 
 def fa_strerror(code):
@@ -258,17 +270,19 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
 def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=None, dk=None, dv=None,
              workspace=None, stream=None):
     """Gradients (dq, dk, dv) of the attention forward, from its outputs o and lse and the output
-    gradient do. q, k, v, o, do, dq, dk, dv: contiguous device tensors [B, H, N, D] of one dtype
-    (bfloat16 or float16); lse: contiguous float32 [B, H, N]. causal, scale and kv_len must be the
-    forward's. workspace: None (allocated here) or a device tensor of at least
-    fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte aligned."""
+    gradient do. q, k, v, o, do, dq, dk, dv: device tensors [B, H, N, D] of one dtype (bfloat16 or
+    float16), any strides with a contiguous last dimension (e.g. [B, N, H, D] storage transposed;
+    a zero head stride on k and v shares one K/V head, and dk, dv are then per query head);
+    lse: contiguous float32 [B, H, N]. causal, scale and kv_len must be the forward's. workspace:
+    None (allocated here) or a device tensor of at least fa_bwd_workspace_bytes(B, H, N, D) bytes,
+    256-byte aligned."""
     ts = (q, k, v, o, do)
     if q.dtype not in (torch.bfloat16, torch.float16) or any(t.dtype != q.dtype for t in ts):
         raise TypeError("q, k, v, o, do must share one dtype among bfloat16, float16")
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
         raise ValueError("q, k, v, o, do must be [B, H, N, D] of one shape")
-    if not all(t.is_cuda and t.is_contiguous() for t in ts):
-        raise ValueError("q, k, v, o, do must be contiguous device tensors")
+    if not all(t.is_cuda and (t.stride(3) == 1 or t.shape[3] <= 1) for t in ts):
+        raise ValueError("q, k, v, o, do must be device tensors with a contiguous last dimension")
     B, H, N, D = q.shape
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
@@ -279,8 +293,8 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=No
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for t in (dq, dk, dv):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("dq, dk, dv must be contiguous device tensors shaped and typed like q")
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or (t.stride(3) != 1 and t.shape[3] > 1):
+            raise ValueError("dq, dk, dv must be device tensors shaped and typed like q, last dimension contiguous")
     need = fa_bwd_workspace_bytes(B, H, N, D)
     if need < 0:
         raise ValueError("sizes too large")
@@ -289,10 +303,13 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=No
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     kv_dev = _kv_len_device(kv_len, B, N, dev)
+    every = (q, k, v, o, do, dq, dk, dv)
+    strides = None if all(t.is_contiguous() for t in every) else [x for t in every for x in t.stride()[:3]]
     with torch.cuda.device(dev):
-        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, float(scale), 1 if causal else 0,
-                    0 if kv_dev is None else kv_dev.data_ptr(), _TORCH_DTYPE[q.dtype], workspace.data_ptr(),
-                    workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+        rc = fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, strides, float(scale),
+                            1 if causal else 0, 0 if kv_dev is None else kv_dev.data_ptr(), _TORCH_DTYPE[q.dtype],
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream_handle(stream, dev))
     _check(rc)
     return dq, dk, dv

@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
 // bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
@@ -364,37 +364,57 @@ extern "C" int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64
   return bwd_stats_bytes(B * H, N);
 }
 
-extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
-                      void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
-                      int causal, const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
-                      void* stream) {
-  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
-  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
-  if (!bwd_supported(dtype, D)) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_ARG;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-  const int64_t lim = INT64_MAX / 16;
-  if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
-  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+namespace {
+
+// Checks and launch shared by fa_bwd and fa_bwd_strided. `st` holds the 8 tensors' strides in
+// the order Q, K, V, O, dO, dQ, dK, dV.
+int bwd_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+               void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, const int64_t st[8][3],
+               float scale, int causal, const int32_t* kv_len, int dtype, void* workspace,
+               int64_t workspace_bytes, void* stream, bool contiguous) {
   const int64_t need = fa_bwd_workspace_bytes(B, H, N, D);
   if (need < 0) return FA_ERR_SHAPE;
+  // The layout is checked before the pointers (it does not depend on them).
+  for (int t = 0; t < 8; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      if (st[t][i] < 0) return FA_ERR_ARG;
+      if ((st[t][i] * 2) % 16 != 0) return FA_ERR_ALIGN;
+    }
+    if (max_offset(B, H, N, D, st[t]) < 0) return FA_ERR_SHAPE;
+  }
+  for (int t = 5; t < 8; ++t)
+    if (!non_overlapping(B, H, N, D, st[t])) return FA_ERR_ARG;
+  // Tiles of Q, dO, K and V are copied with 32-bit per-lane offsets over up to 128 rows.
+  for (int t : {0, 1, 2, 4})
+    if (st[t][2] * 2 > (int64_t(1) << 31) / 128) return FA_ERR_SHAPE;
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_NULL;
   for (const void* ptr : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (misaligned(ptr, 16)) return FA_ERR_ALIGN;
   if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4)) || misaligned(workspace, 256)) return FA_ERR_ALIGN;
   if (workspace_bytes < need) return FA_ERR_ARG;
-  // Outputs (and the workspace, which is written) must not overlap each other or any input.
   const int64_t tb = B * H * N * D * 2;
-  const void* outs[4] = {dQ, dK, dV, workspace};
-  const int64_t out_b[4] = {tb, tb, tb, need};
-  const void* ins[6] = {Q, K, V, O, dO, LSE};
-  const int64_t in_b[6] = {tb, tb, tb, tb, tb, B * H * N * 4};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return FA_ERR_ARG;
-    for (int j = i + 1; j < 4; ++j)
-      if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return FA_ERR_ARG;
+  if (contiguous) {
+    // Outputs (and the workspace, which is written) must not overlap each other or any input.
+    const void* outs[4] = {dQ, dK, dV, workspace};
+    const int64_t out_b[4] = {tb, tb, tb, need};
+    const void* ins[6] = {Q, K, V, O, dO, LSE};
+    const int64_t in_b[6] = {tb, tb, tb, tb, tb, B * H * N * 4};
+    for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < 6; ++j)
+        if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return FA_ERR_ARG;
+      for (int j = i + 1; j < 4; ++j)
+        if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return FA_ERR_ARG;
+    }
+  } else {
+    // Strided views may interleave (e.g. dQ, dK, dV as slices of one packed tensor), so only
+    // an output that starts at an input, another output or the workspace is rejected here.
+    const void* outs[3] = {dQ, dK, dV};
+    for (int i = 0; i < 3; ++i) {
+      for (const void* in : {Q, K, V, O, dO, (const void*)LSE, (const void*)workspace})
+        if (outs[i] == in) return FA_ERR_ARG;
+      for (int j = i + 1; j < 3; ++j)
+        if (outs[i] == outs[j]) return FA_ERR_ARG;
+    }
   }
   fa::BwdParams p;
   p.q = Q;
@@ -406,6 +426,8 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   p.dq = dQ;
   p.dk = dK;
   p.dv = dV;
+  fa::Strides3* ps[8] = {&p.st_q, &p.st_k, &p.st_v, &p.st_o, &p.st_do, &p.st_dq, &p.st_dk, &p.st_dv};
+  for (int t = 0; t < 8; ++t) *ps[t] = fa::Strides3{st[t][0], st[t][1], st[t][2]};
   p.stats = static_cast<float*>(workspace);
   p.kv_len = kv_len;
   p.H = H;
@@ -415,6 +437,59 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   p.causal = causal;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return dtype == FA_BF16 ? dispatch_bwd<__bf16>(D, p, B, H, N, s) : dispatch_bwd<_Float16>(D, p, B, H, N, s);
+}
+
+int bwd_precheck(int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal, int dtype, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
+  if (!bwd_supported(dtype, D)) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  const int64_t lim = INT64_MAX / 16;
+  if (B > lim / H || B * H > lim / N || B * H * N > lim / D) return FA_ERR_SHAPE;
+  if (N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                      void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
+                      int causal, const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+  bool empty;
+  const int rc = bwd_precheck(B, H, N, D, scale, causal, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  int64_t st[8][3];
+  for (int t = 0; t < 8; ++t) {
+    st[t][0] = H * N * D;
+    st[t][1] = N * D;
+    st[t][2] = D;
+  }
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, st, scale, causal, kv_len, dtype, workspace,
+                    workspace_bytes, stream, true);
+}
+
+extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                              const void* dO, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
+                              int64_t D, const int64_t* strides, float scale, int causal, const int32_t* kv_len,
+                              int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!strides)
+    return fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype, workspace,
+                  workspace_bytes, stream);
+  bool empty;
+  const int rc = bwd_precheck(B, H, N, D, scale, causal, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  int64_t st[8][3];
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) st[t][i] = strides[3 * t + i];
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, st, scale, causal, kv_len, dtype, workspace,
+                    workspace_bytes, stream, false);
 }
 
 extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,

@@ -42,16 +42,23 @@
 
 namespace fa {
 
+// Element strides of the batch, head and token dimensions of one [B][H][N][D] tensor (the head
+// dimension D is contiguous): element (b, h, n, d) lives at X + b*b_ + h*h_ + n*n_ + d.
+struct Strides3 {
+  int64_t b, h, n;
+};
+
 struct BwdParams {
-  const void* q;      // contiguous [B][H][N][D]
+  const void* q;      // [B][H][N][D], strided as st_q, ...
   const void* k;
   const void* v;
   const void* o;
   const void* dout;
-  const float* lse;   // [B][H][N], natural log
-  void* dq;           // outputs, contiguous [B][H][N][D]
+  const float* lse;   // contiguous [B][H][N], natural log
+  void* dq;           // outputs
   void* dk;
   void* dv;
+  Strides3 st_q, st_k, st_v, st_o, st_do, st_dq, st_dk, st_dv;
   float* stats;       // [B*H][ceil(N/64)][128] floats: 64 exponent offsets, then 64 Delta values
   const int32_t* kv_len;
   int64_t H, N;
@@ -82,7 +89,8 @@ __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh)
 }
 
 // Per-lane copy plan of a [rows][D] tile into LDS, 1 KB per copy instruction: copy i of this
-// wave fills rows (wave*LPW + i)*RPB + lane/CPR, physical chunk lane%CPR.
+// wave fills LDS rows (wave*LPW + i)*RPB + lane/CPR, physical chunk lane%CPR. In global memory
+// the rows are `stride` bytes apart (the token stride; below 2^31 / ROWS, checked by the host).
 template <int D, int ROWS, int NW>
 struct TilePlan {
   static constexpr int ROWB = D * 2;
@@ -92,24 +100,24 @@ struct TilePlan {
   static constexpr int RPB = 1024 / ROWB;
   static_assert(TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
   int row[LPW];
-  unsigned off[LPW];  // byte offset of this lane's 16 bytes within the tile in global memory
+  unsigned chunk[LPW];  // byte offset, within the row, of the logical chunk this lane copies
   __device__ __forceinline__ TilePlan(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int j = (wave * LPW + i) * RPB + lane / CPR;
       row[i] = j;
-      off[i] = j * ROWB + ((lane % CPR) ^ swz_u<D>(j)) * 16;
+      chunk[i] = ((lane % CPR) ^ swz_u<D>(j)) * 16;
     }
   }
-  // Copy rows [r0, r0 + ROWS) of the tensor at `src` (n rows) into `dst`; rows past n read
-  // row n-1 instead.
-  __device__ __forceinline__ void issue(const unsigned char* src, int r0, int n, unsigned dst, int wave) const {
-    const unsigned char* t = src + (int64_t)r0 * ROWB;
+  // Copy rows [r0, r0 + ROWS) of the tensor at `src` (n rows, `stride` bytes apart) into `dst`;
+  // rows past n read row n-1 instead.
+  __device__ __forceinline__ void issue(const unsigned char* src, unsigned stride, int r0, int n, unsigned dst,
+                                        int wave) const {
+    const unsigned char* t = src + (int64_t)r0 * stride;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int over = r0 + row[i] - (n - 1);
-      const unsigned back = over > 0 ? (unsigned)over * ROWB : 0u;
-      lds_copy16(t, off[i] - back, dst + (wave * LPW + i) * 1024);
+      const int rr = min(row[i], n - 1 - r0);
+      lds_copy16(t, (unsigned)rr * stride + chunk[i], dst + (wave * LPW + i) * 1024);
     }
   }
   // Zero this lane's slots of rows at or past `lim` (tile-relative).
@@ -166,13 +174,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int qt = decode_tile(p, blockIdx.x, &bh);
   if (p.causal) qt = p.n_tiles - 1 - qt;  // longest query tiles first
   const int n = (int)p.N;
-  const int64_t base = (int64_t)bh * n * D;
-  const T* Qh = reinterpret_cast<const T*>(p.q) + base;
-  const T* Oh = reinterpret_cast<const T*>(p.o) + base;
-  const T* dOh = reinterpret_cast<const T*>(p.dout) + base;
-  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + base);
-  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + base);
-  T* dQh = reinterpret_cast<T*>(p.dq) + base;
+  const int64_t b_ = bh / p.H, h_ = bh % p.H;
+  const T* Qh = reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h;
+  const T* Oh = reinterpret_cast<const T*>(p.o) + b_ * p.st_o.b + h_ * p.st_o.h;
+  const T* dOh = reinterpret_cast<const T*>(p.dout) + b_ * p.st_do.b + h_ * p.st_do.h;
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + b_ * p.st_k.b + h_ * p.st_k.h);
+  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + b_ * p.st_v.b + h_ * p.st_v.h);
+  T* dQh = reinterpret_cast<T*>(p.dq) + b_ * p.st_dq.b + h_ * p.st_dq.h;
+  const unsigned ksn = (unsigned)(p.st_k.n * 2), vsn = (unsigned)(p.st_v.n * 2);
 
   const int q0 = qt * BR;
   const int qw = q0 + 32 * wave;
@@ -196,9 +205,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
     if (qrow < n) {
-      qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * D + 16 * s + 8 * g);
-      dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * D + 16 * s + 8 * g);
-      const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * D + 16 * s + 8 * g);
+      qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * p.st_q.n + 16 * s + 8 * g);
+      dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * p.st_do.n + 16 * s + 8 * g);
+      const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * p.st_o.n + 16 * s + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)dof[s][e], (float)of[e], dsum);
     } else {
@@ -228,8 +237,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto issue = [&](int t, int buf) {
     const unsigned kl = lds_address(lds + buf * 2 * TILEB);
-    plan.issue(Kh, t * BC, n, kl, wave);
-    plan.issue(Vh, t * BC, n, kl + TILEB, wave);
+    plan.issue(Kh, ksn, t * BC, n, kl, wave);
+    plan.issue(Vh, vsn, t * BC, n, kl + TILEB, wave);
   };
   if (ntiles > 0) issue(0, 0);
 
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         T o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (T)(acc[dt][4 * a4 + e] * p.scale);
-        *reinterpret_cast<uint2*>(dQh + (int64_t)qrow * D + 32 * dt + 8 * a4 + 4 * g) = *reinterpret_cast<const uint2*>(o4);
+        *reinterpret_cast<uint2*>(dQh + (int64_t)qrow * p.st_dq.n + 32 * dt + 8 * a4 + 4 * g) = *reinterpret_cast<const uint2*>(o4);
       }
   }
 }
@@ -366,13 +375,14 @@ void bwd_dkdv_kernel(BwdParams p) {
   int bh;
   const int kt = decode_tile(p, blockIdx.x, &bh);  // causal: key tile 0 has the most work
   const int n = (int)p.N;
-  const int64_t base = (int64_t)bh * n * D;
-  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + base);
-  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + base);
-  const T* Kh = reinterpret_cast<const T*>(p.k) + base;
-  const T* Vh = reinterpret_cast<const T*>(p.v) + base;
-  T* dKh = reinterpret_cast<T*>(p.dk) + base;
-  T* dVh = reinterpret_cast<T*>(p.dv) + base;
+  const int64_t b_ = bh / p.H, h_ = bh % p.H;
+  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h);
+  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + b_ * p.st_do.b + h_ * p.st_do.h);
+  const T* Kh = reinterpret_cast<const T*>(p.k) + b_ * p.st_k.b + h_ * p.st_k.h;
+  const T* Vh = reinterpret_cast<const T*>(p.v) + b_ * p.st_v.b + h_ * p.st_v.h;
+  T* dKh = reinterpret_cast<T*>(p.dk) + b_ * p.st_dk.b + h_ * p.st_dk.h;
+  T* dVh = reinterpret_cast<T*>(p.dv) + b_ * p.st_dv.b + h_ * p.st_dv.h;
+  const unsigned qsn = (unsigned)(p.st_q.n * 2), osn = (unsigned)(p.st_do.n * 2);
   const int n64 = (n + kStatRows - 1) / kStatRows;
   const unsigned char* Sh = reinterpret_cast<const unsigned char*>(p.stats + (int64_t)bh * n64 * (2 * kStatRows));
 
@@ -396,8 +406,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
     if (key < kvl) {
-      kf[s] = *reinterpret_cast<const frag*>(Kh + (int64_t)key * D + 16 * s + 8 * g);
-      vf[s] = *reinterpret_cast<const frag*>(Vh + (int64_t)key * D + 16 * s + 8 * g);
+      kf[s] = *reinterpret_cast<const frag*>(Kh + (int64_t)key * p.st_k.n + 16 * s + 8 * g);
+      vf[s] = *reinterpret_cast<const frag*>(Vh + (int64_t)key * p.st_v.n + 16 * s + 8 * g);
     } else {
       kf[s] = frag{};
       vf[s] = frag{};
@@ -419,8 +429,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   auto issue = [&](int t, int buf) {
     const unsigned ql = lds_address(lds + buf * BUFB);
-    plan.issue(Qh, t * BQ, n, ql, wave);
-    plan.issue(dOh, t * BQ, n, ql + TILEB, wave);
+    plan.issue(Qh, qsn, t * BQ, n, ql, wave);
+    plan.issue(dOh, osn, t * BQ, n, ql + TILEB, wave);
     if (wave == 0) lds_copy16(Sh + (int64_t)t * (2 * kStatRows) * 4, stat_off, ql + 2 * TILEB);
   };
   if (t0 < nqt) issue(t0, 0);
@@ -534,9 +544,9 @@ void bwd_dkdv_kernel(BwdParams p) {
           k4[e] = (T)(dka[dt][4 * a4 + e] * p.scale);
           v4[e] = (T)dva[dt][4 * a4 + e];
         }
-        const int64_t off = (int64_t)key * D + 32 * dt + 8 * a4 + 4 * g;
-        *reinterpret_cast<uint2*>(dKh + off) = *reinterpret_cast<const uint2*>(k4);
-        *reinterpret_cast<uint2*>(dVh + off) = *reinterpret_cast<const uint2*>(v4);
+        const int dd = 32 * dt + 8 * a4 + 4 * g;
+        *reinterpret_cast<uint2*>(dKh + (int64_t)key * p.st_dk.n + dd) = *reinterpret_cast<const uint2*>(k4);
+        *reinterpret_cast<uint2*>(dVh + (int64_t)key * p.st_dv.n + dd) = *reinterpret_cast<const uint2*>(v4);
       }
   }
 }
@@ -581,13 +591,15 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
   int bh;
   const int kt = decode_tile(p, blockIdx.x, &bh);
   const int n = (int)p.N;
-  const int64_t base = (int64_t)bh * n * D;
-  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + base);
-  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + base);
-  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + base);
-  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + base);
-  T* dKh = reinterpret_cast<T*>(p.dk) + base;
-  T* dVh = reinterpret_cast<T*>(p.dv) + base;
+  const int64_t b_ = bh / p.H, h_ = bh % p.H;
+  const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h);
+  const unsigned char* dOh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.dout) + b_ * p.st_do.b + h_ * p.st_do.h);
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.k) + b_ * p.st_k.b + h_ * p.st_k.h);
+  const unsigned char* Vh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.v) + b_ * p.st_v.b + h_ * p.st_v.h);
+  T* dKh = reinterpret_cast<T*>(p.dk) + b_ * p.st_dk.b + h_ * p.st_dk.h;
+  T* dVh = reinterpret_cast<T*>(p.dv) + b_ * p.st_dv.b + h_ * p.st_dv.h;
+  const unsigned qsn = (unsigned)(p.st_q.n * 2), osn = (unsigned)(p.st_do.n * 2);
+  const unsigned ksn = (unsigned)(p.st_k.n * 2), vsn = (unsigned)(p.st_v.n * 2);
   const int n64 = (n + kStatRows - 1) / kStatRows;
   const unsigned char* Sh = reinterpret_cast<const unsigned char*>(p.stats + (int64_t)bh * n64 * (2 * kStatRows));
 
@@ -612,13 +624,13 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
   const unsigned stat_off = (unsigned)(lane & 31) * 16;
   auto issue = [&](int t, int buf) {
     const unsigned ql = lds_address(qbuf + buf * BUFB);
-    qplan.issue(Qh, t * BQ, n, ql, wave);
-    qplan.issue(dOh, t * BQ, n, ql + QTB, wave);
+    qplan.issue(Qh, qsn, t * BQ, n, ql, wave);
+    qplan.issue(dOh, osn, t * BQ, n, ql + QTB, wave);
     if (wave == 0) lds_copy16(Sh + (int64_t)t * (2 * kStatRows) * 4, stat_off, ql + 2 * QTB);
   };
   if (t0 < nqt) {
-    kplan.issue(Kh, k0, n, lds_address(kb), wave);
-    kplan.issue(Vh, k0, n, lds_address(vb), wave);
+    kplan.issue(Kh, ksn, k0, n, lds_address(kb), wave);
+    kplan.issue(Vh, vsn, k0, n, lds_address(vb), wave);
     issue(t0, 0);
     wait_vmem();
     // Keys at or past kv_len may hold anything: zero them so 0 * garbage cannot reach dK, dV.
@@ -744,9 +756,9 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
         k4[e] = (T)((dka[dt][4 * a4 + e] + ks[e]) * p.scale);
         v4[e] = (T)(dva[dt][4 * a4 + e] + vs[e]);
       }
-      const int64_t off = (int64_t)key * D + 32 * dt + 8 * a4 + 4 * g;
-      *reinterpret_cast<uint2*>(dKh + off) = *reinterpret_cast<const uint2*>(k4);
-      *reinterpret_cast<uint2*>(dVh + off) = *reinterpret_cast<const uint2*>(v4);
+      const int dd = 32 * dt + 8 * a4 + 4 * g;
+      *reinterpret_cast<uint2*>(dKh + (int64_t)key * p.st_dk.n + dd) = *reinterpret_cast<const uint2*>(k4);
+      *reinterpret_cast<uint2*>(dVh + (int64_t)key * p.st_dv.n + dd) = *reinterpret_cast<const uint2*>(v4);
     }
 }
 

@@ -211,6 +211,28 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
            const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
            void* stream);
 
+/*
+ * fa_bwd_strided - fa_bwd over strided tensors: the views callers usually hold (for example
+ * [B][N][H][D] storage seen as [B][H][N][D]) without a copy. The arithmetic is that of fa_bwd.
+ *
+ * strides : host pointer to 24 int64 element strides, or NULL for contiguous [B][H][N][D]
+ *           (then exactly fa_bwd): { q_b, q_h, q_n,  k_b, k_h, k_n,  v_b, v_h, v_n,
+ *           o_b, o_h, o_n,  do_b, do_h, do_n,  dq_b, dq_h, dq_n,  dk_b, dk_h, dk_n,
+ *           dv_b, dv_h, dv_n }. Element (b, h, n, d) of X lives at X + b*x_b + h*x_h + n*x_n + d.
+ *           Every stride must be >= 0 and a multiple of 16 bytes; the token strides of Q, K, V
+ *           and dO may not exceed 16 MiB. Inputs may overlap themselves (a zero head stride on K
+ *           and V shares one K/V head among all query heads; dK and dV are then the gradients
+ *           per query head, which the caller sums over the heads that share one). dQ, dK and dV
+ *           must not overlap themselves (FA_ERR_ARG), nor each other or any input; only an
+ *           output starting at an input, another output or the workspace is detected.
+ * LSE and the workspace stay contiguous. Other arguments and errors as fa_bwd.
+ */
+int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                   const void* dO, void* dQ, void* dK, void* dV,
+                   int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
+                   float scale, int causal, const int32_t* kv_len, int dtype, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);
 

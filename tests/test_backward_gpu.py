@@ -212,3 +212,52 @@ def test_backward_full_size_sampled():
             T = rounding_bound(*one, causal, None, "bf16")
             for gg, rr, tt, name in zip((dq, dk, dv), ref, T, ("dQ", "dK", "dV")):
                 compare_grad(gg[b:b + 1, h:h + 1], rr, tt, "bf16", f"full {name} b={b} h={h}")
+
+
+def test_backward_strided_layouts():
+    """[B, N, H, D] storage seen as [B, H, N, D] for every input, dQ/dK/dV written into one packed
+    [B, N, 3, H, D] tensor: bit-identical to the contiguous call (strides change addressing only),
+    and within the bound of the oracle."""
+    B, H, N, D = 2, 3, 333, 128
+    x = generate(B, H, N, D, "bf16", causal=True, seed=401)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=402)
+    q, k, v, dO = (t.to(DEV) for t in (x.q, x.k, x.v, do))
+    o, lse = fa.forward(q, k, v, causal=True, scale=x.scale)
+    ref_grads = fa.backward(q, k, v, o, lse, dO, causal=True, scale=x.scale)
+    bnhd = lambda t: t.transpose(1, 2).contiguous().transpose(1, 2)
+    qs, ks, vs, os_, dos = (bnhd(t) for t in (q, k, v, o, dO))
+    packed = torch.full((B, N, 3, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dq, dk, dv = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    say("bwd strided: BNHD inputs, packed outputs")
+    fa.backward(qs, ks, vs, os_, lse, dos, causal=True, scale=x.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for a, b_, name in zip((dq, dk, dv), ref_grads, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b_), f"strided {name} differs from the contiguous call"
+    args = (to_f64(x.q), to_f64(x.k), to_f64(x.v), to_f64(do), x.scale)
+    ref = oracle.attention_grad(*args, causal=True)
+    T = rounding_bound(*args, True, None, "bf16")
+    for g, r, t, name in zip((dq, dk, dv), ref, T, ("dQ", "dK", "dV")):
+        compare_grad(g, r, t, "bf16", f"strided {name}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_shared_kv_head(D):
+    """One K/V head shared by every query head (zero head stride): dK and dV come out per query
+    head and equal the gradients of attention with that K/V repeated in every head."""
+    B, H, N = 2, 4, 300
+    x = generate(B, H, N, D, "bf16", causal=False, seed=403)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=404)
+    q, dO = x.q.to(DEV), do.to(DEV)
+    k1 = x.k[:, :1].to(DEV).expand(B, H, N, D)
+    v1 = x.v[:, :1].to(DEV).expand(B, H, N, D)
+    o, lse = fa.forward(q, k1, v1, causal=False, scale=x.scale)
+    say(f"bwd shared kv head D={D}")
+    dq, dk, dv = fa.backward(q, k1, v1, o, lse, dO, causal=False, scale=x.scale)
+    torch.cuda.synchronize()
+    kk = np.repeat(to_f64(x.k[:, :1]), H, axis=1)
+    vv = np.repeat(to_f64(x.v[:, :1]), H, axis=1)
+    args = (to_f64(x.q), kk, vv, to_f64(do), x.scale)
+    ref = oracle.attention_grad(*args, causal=False)
+    T = rounding_bound(*args, False, None, "bf16")
+    for g, r, t, name in zip((dq, dk, dv), ref, T, ("dQ", "dK", "dV")):
+        compare_grad(g, r, t, "bf16", f"shared kv {name}")

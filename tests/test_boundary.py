@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 4
+    assert fa.fa_abi_version() == 5
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -333,3 +333,43 @@ def test_bwd_overlap_rejected():
 
 def test_bwd_empty_is_noop():
     assert call_bwd(N=0, Q=0, K=0, V=0, O=0, LSE=0, dO=0, dQ=0, dK=0, dV=0, ws=0) == binding.FA_OK
+
+
+CONTIG_B = [3 * 8 * 64, 8 * 64, 64] * 8     # [2, 3, 8, 64] contiguous, for all 8 tensors
+
+
+def call_bwd_strided(strides, **kw):
+    a = dict(BG)
+    a.update(kw)
+    return fa.fa_bwd_strided(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dO"], a["dQ"], a["dK"], a["dV"], a["B"],
+                             a["H"], a["N"], a["D"], strides, a["scale"], a["causal"], a["kv_len"], a["dtype"],
+                             a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_bwd_strided_negative_and_misaligned(i):
+    s = list(CONTIG_B)
+    s[i] = -s[i]
+    assert call_bwd_strided(s) == binding.FA_ERR_ARG
+    s = list(CONTIG_B)
+    s[i] += 4
+    assert call_bwd_strided(s) == binding.FA_ERR_ALIGN
+
+
+def test_bwd_strided_layout_rules():
+    # overlapping outputs (dQ head stride 0) are rejected; shared K/V heads pass the layout
+    # checks (and stop at the NULL pointer)
+    s = list(CONTIG_B)
+    s[15 + 1] = 0
+    assert call_bwd_strided(s) == binding.FA_ERR_ARG
+    s = list(CONTIG_B)
+    s[3 + 1] = 0
+    s[6 + 1] = 0
+    assert call_bwd_strided(s, Q=0) == binding.FA_ERR_NULL
+    s = list(CONTIG_B)
+    s[2] = 1 << 24                                # Q token stride of 32 MiB (limit 16 MiB)
+    assert call_bwd_strided(s) == binding.FA_ERR_SHAPE
+    s = list(CONTIG_B)
+    assert call_bwd_strided(s, dK=BG["dQ"]) == binding.FA_ERR_ARG   # two outputs at one address
+    assert call_bwd_strided(s, dV=BG["K"]) == binding.FA_ERR_ARG    # output on an input
+    assert call_bwd_strided(None, N=0, Q=0) == binding.FA_OK
