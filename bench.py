@@ -157,6 +157,9 @@ def main():
     ap.add_argument("--shape", default=None,
                     help="B,H,N,D,dtype,causal: a seeded synthetic workload of this shape instead of a named one "
                          "(the recipe of the named workloads, seed 7)")
+    ap.add_argument("--gemm", type=int, default=0,
+                    help="instead of attention, time a bf16 N x N x N matrix product through torch (the vendor "
+                         "GEMM library): the matrix cores' practical throughput under the same power and clock")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes per step "
                          "(scale reference for the HBM byte counters)")
@@ -175,6 +178,29 @@ def main():
     import exact_tiled_attention_23_amd as fa
     from exact_tiled_attention_23_amd.workloads import (HEADLINE, WORKLOADS, Workload, generate_grad_output,
                                                         generate_workload)
+
+    if args.gemm:
+        n = args.gemm
+        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda:0")
+        bm = torch.randn(n, n, dtype=torch.bfloat16, device="cuda:0")
+        c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(args.warmup):
+            torch.matmul(a, bm, out=c)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, bm, out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        flops = 2.0 * n ** 3
+        print(json.dumps({"calibration": "bf16 GEMM", "n": n, "steps": args.steps,
+                          "tflops_median": round(flops / float(np.median(ms)) / 1e9, 1),
+                          "tflops_best": round(flops / min(ms) / 1e9, 1),
+                          "ms_median": round(float(np.median(ms)), 4)}))
+        return
 
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
