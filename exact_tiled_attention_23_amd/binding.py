@@ -313,3 +313,57 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=No
                             _stream_handle(stream, dev))
     _check(rc)
     return dq, dk, dv
+
+
+class FlashAttention:
+    """Object interface in the shape of the pages' one ("vectorized-flash-attention-kernel",
+    Constructor options; Key design decision 4): options at construction, forward(q, k, v)
+    returning O while keeping the per-row statistics (LSE), and backward(do) rebuilding the
+    gradients from them. The tile size is fixed per head dimension by the kernels, and the
+    statistics are always kept (the forward always returns LSE)."""
+
+    def __init__(self, causal=True, softmax_scale=None, kv_len=None):
+        self.causal = causal
+        self.softmax_scale = softmax_scale
+        self.kv_len = kv_len
+        self._saved = None
+
+    def forward(self, q, k, v):
+        o, lse = forward(q, k, v, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len)
+        self._saved = (q, k, v, o, lse)
+        return o
+
+    @property
+    def lse(self):
+        """Natural-log softmax denominators of the last forward, [B, H, N] float32."""
+        return None if self._saved is None else self._saved[4]
+
+    def backward(self, do):
+        if self._saved is None:
+            raise RuntimeError("backward() needs a forward() first")
+        q, k, v, o, lse = self._saved
+        return backward(q, k, v, o, lse, do, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len)
+
+
+class _AttentionFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale, kv_len):
+        o, lse = forward(q, k, v, causal=causal, scale=scale, kv_len=kv_len)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale, ctx.kv_len = causal, scale, kv_len
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        if do.stride(-1) != 1:
+            do = do.contiguous()
+        dq, dk, dv = backward(q, k, v, o, lse, do, causal=ctx.causal, scale=ctx.scale, kv_len=ctx.kv_len)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, causal=True, scale=None, kv_len=None):
+    """Differentiable attention for torch autograd: forward() now, backward() (fa_bwd) when the
+    graph is differentiated. q, k, v: bfloat16/float16 device tensors [B, H, N, D], D <= 128 for
+    the backward; see forward() for the options."""
+    return _AttentionFunction.apply(q, k, v, causal, scale, kv_len)

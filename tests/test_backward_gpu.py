@@ -261,3 +261,28 @@ def test_backward_shared_kv_head(D):
     T = rounding_bound(*args, False, None, "bf16")
     for g, r, t, name in zip((dq, dk, dv), ref, T, ("dQ", "dK", "dV")):
         compare_grad(g, r, t, "bf16", f"shared kv {name}")
+
+
+def test_autograd_and_object_interface():
+    """attention() under torch autograd and the FlashAttention object both give the oracle's
+    gradients (the same kernels behind them)."""
+    B, H, N, D = 1, 2, 200, 64
+    x = generate(B, H, N, D, "bf16", causal=True, seed=405)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=406)
+    q, k, v = (t.to(DEV).requires_grad_(True) for t in (x.q, x.k, x.v))
+    say("autograd attention")
+    o = fa.attention(q, k, v, causal=True, scale=x.scale)
+    (o.float() * do.to(DEV).float()).sum().backward()
+    torch.cuda.synchronize()
+    args = (to_f64(x.q), to_f64(x.k), to_f64(x.v), to_f64(do), x.scale)
+    ref = oracle.attention_grad(*args, causal=True)
+    T = rounding_bound(*args, True, None, "bf16")
+    for g, r, t, name in zip((q.grad, k.grad, v.grad), ref, T, ("dQ", "dK", "dV")):
+        compare_grad(g, r, t, "bf16", f"autograd {name}")
+    fla = fa.FlashAttention(causal=True, softmax_scale=x.scale)
+    o2 = fla.forward(x.q.to(DEV), x.k.to(DEV), x.v.to(DEV))
+    assert torch.equal(o2, o.detach()) and fla.lse.shape == (B, H, N)
+    grads = fla.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    for a, b_ in zip(grads, (q.grad, k.grad, v.grad)):
+        assert torch.equal(a, b_)
