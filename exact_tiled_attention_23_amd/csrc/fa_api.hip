@@ -1,5 +1,6 @@
-// C ABI of the attention forward (declared in include/fa.h): argument checks and
-// kernel dispatch. Every check runs before any HIP call; the library keeps no state.
+// C ABI of the attention forward, key-split forward, partial-state merge and backward
+// (declared in include/fa.h): argument checks and kernel dispatch. Every check runs before
+// any kernel launch; the library keeps no state and allocates nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -226,9 +227,9 @@ extern "C" const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid sizes (negative, or too large for the kernel's indexing)";
-    case FA_ERR_UNSUPPORTED: return "unsupported dtype (f32, bf16, f16) or head dimension (32, 64, 128; 256 for bf16/f16)";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (forward: f32, bf16, f16 with D 32, 64, 128, and 256 for bf16/f16; backward: bf16, f16 with D 32, 64, 128)";
     case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE and kv_len 4 bytes)";
-    case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, O not aliasing Q, K or V nor itself)";
+    case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown error code";
   }

@@ -27,11 +27,13 @@
 //    registers; it walks the query tiles. S = Q.K^T and dP = dO.V^T give each lane one key
 //    and 16 queries of every 32-query sub-tile (Q and dO rows are read in a permuted order so
 //    that the accumulator is exactly the next product's operand), so P and dS feed
-//    dV^T = dO^T.P and dK^T = Q^T.dS directly.
+//    dV^T = dO^T.P and dK^T = Q^T.dS directly. At D = 128, bwd_dkdv_lds_kernel keeps the
+//    tile's K and V in LDS instead of registers so that two waves fit on each SIMD.
 //
-// Tiles go HBM -> LDS with direct 16-byte copies, double-buffered. Every tile is read both
-// row-wise and by transpose reads, so one XOR swizzle of the 16-byte chunks serves both
-// without bank conflicts (swz_u below).
+// Every tensor is addressed through its own batch, head and token strides (the head
+// dimension contiguous). Tiles go HBM -> LDS with direct 16-byte copies, double-buffered.
+// Every tile is read both row-wise and by transpose reads, so one XOR swizzle of the 16-byte
+// chunks serves both without bank conflicts (swz_u below).
 #pragma once
 
 #include <hip/hip_runtime.h>
