@@ -83,6 +83,21 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def blas_info():
+    """The NumPy build's BLAS library and the BLAS thread pools, for the CPU baseline record."""
+    import numpy as np
+    try:
+        name = np.__config__.CONFIG["Build Dependencies"]["blas"]["name"]
+    except (AttributeError, KeyError, TypeError):
+        name = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        pools = sorted({f"{p['internal_api']}:{p['num_threads']}" for p in threadpool_info()})
+    except ImportError:
+        pools = []
+    return {"numpy": np.__version__, "blas": name, "blas_pools": pools}
+
+
 def cpu_baseline(x, w, heads):
     """The float64 oracle on the first `heads` (batch, head) pairs of the same inputs, all rows."""
     import numpy as np
@@ -116,7 +131,8 @@ def cpu_baseline(x, w, heads):
     flops = 4.0 * w.D * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} query rows, float64",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "workers": cores, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "gflops_fp64": round(flops / dt / 1e9, 1), **blas_info()}
 
 
 def cpu_baseline_backward(x, do, w, heads):
@@ -141,7 +157,7 @@ def cpu_baseline_backward(x, do, w, heads):
     dt = time.perf_counter() - t0
     return {"value": 10.0 * w.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} (batch, head) pairs, all {w.N} query rows, float64",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "affinity_cpus": len(os.sched_getaffinity(0)), **blas_info()}
 
 
 def main():
@@ -157,6 +173,10 @@ def main():
     ap.add_argument("--shape", default=None,
                     help="B,H,N,D,dtype,causal: a seeded synthetic workload of this shape instead of a named one "
                          "(the recipe of the named workloads, seed 7)")
+    ap.add_argument("--cold-bytes", type=int, default=0,
+                    help="write this many bytes of scratch memory between timed launches (e.g. 1 GiB, beyond the "
+                         "256 MB MALL) so each launch finds its inputs outside the caches; value is then the "
+                         "kernel-timed rate")
     ap.add_argument("--gemm", type=int, default=0,
                     help="instead of attention, time a bf16 N x N x N matrix product through torch (the vendor "
                          "GEMM library): the matrix cores' practical throughput under the same power and clock")
@@ -251,9 +271,12 @@ def main():
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     log(f"bench: timing {args.steps} steps")
+    scratch = torch.empty(args.cold_bytes // 4, dtype=torch.float32, device=dev) if args.cold_bytes else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s, e in ev:
+        if scratch is not None:
+            scratch.fill_(1.0)          # evicts the inputs from L2 and MALL; outside the events
         s.record(stream)
         step()
         e.record(stream)
@@ -268,6 +291,8 @@ def main():
     elt = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_kernel_s / 1e12
+    if args.cold_bytes:
+        value = achieved
     peak = PEAK_TFLOPS[w.dtype]
     nbytes = algorithmic_bytes(w, x.kv_len, elt)
     if args.backward:
@@ -299,6 +324,7 @@ def main():
                        "kv_len": None if x.kv_len is None else [int(t) for t in x.kv_len],
                        "parallelism": "single GPU"},
             "pct_of_peak": round(100.0 * value / peak, 2),
+            "cold_cache_bytes": args.cold_bytes or None,
             "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
