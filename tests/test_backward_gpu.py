@@ -286,3 +286,19 @@ def test_autograd_and_object_interface():
     torch.cuda.synchronize()
     for a, b_ in zip(grads, (q.grad, k.grad, v.grad)):
         assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_backward_large_logits(dtype):
+    """Rows of Q scaled by U[1, 100) (the padded workload's recipe): logits in the hundreds, P
+    rebuilt from exponent offsets of the same size, kv_len padding with an empty batch."""
+    N, D = 400, 64
+    x = generate(3, 2, N, D, dtype, causal=True, seed=407, padding=True, q_row_scale=True)
+    do = generate_grad_output(3, 2, N, D, dtype, seed=408)
+    say(f"bwd large logits {dtype} kv_len={x.kv_len.tolist()}")
+    got = run_bwd(x, do, kv_len=x.kv_len)
+    args = (to_f64(x.q), to_f64(x.k), to_f64(x.v), to_f64(do), x.scale)
+    ref = oracle.attention_grad(*args, causal=True, kv_len=x.kv_len)
+    T = rounding_bound(*args, True, x.kv_len, dtype)
+    for g, r, t, name in zip(got, ref, T, ("dQ", "dK", "dV")):
+        compare_grad(g, r, t, dtype, f"large logits {name}")
