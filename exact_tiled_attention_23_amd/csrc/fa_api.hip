@@ -25,6 +25,7 @@ constexpr int kBlockKV = 64;   // keys per K/V tile
 template <int D> struct Shape16;
 template <> struct Shape16<32> { static constexpr int BC = 128, NW = 4, WPE = 2; };
 template <> struct Shape16<64> { static constexpr int BC = 128, NW = 4, WPE = 2; };
+template <> struct Shape16<96> { static constexpr int BC = 64, NW = 8, WPE = 2; };
 template <> struct Shape16<128> { static constexpr int BC = 64, NW = 8, WPE = 2; };
 template <> struct Shape16<256> { static constexpr int BC = 64, NW = 4, WPE = 1; };
 constexpr int kMaxBC = 128;  // largest key tile: bounds the per-lane 32-bit copy offsets
@@ -95,6 +96,7 @@ int dispatch_d(int64_t D, const void* Q, const void* K, const void* V, void* O, 
   switch (D) {
     case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
     case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+    case 96: return launch<T, 96>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
     case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
     default:
       if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
@@ -132,6 +134,7 @@ int dispatch_merge(int64_t D, const float* part_o, const float* part_lse, int S,
   switch (D) {
     case 32: return launch_merge<T, 32>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
     case 64: return launch_merge<T, 64>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
+    case 96: return launch_merge<T, 96>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
     case 128: return launch_merge<T, 128>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
     default: return launch_merge<T, 256>(part_o, part_lse, S, B, H, N, O, o_st, LSE, stream);
   }
@@ -176,6 +179,7 @@ int suggest_splits_d(int64_t D, int64_t B, int64_t H, int64_t N, int causal, int
   switch (D) {
     case 32: return suggest_splits<T, 32>(B, H, N, causal, n_splits);
     case 64: return suggest_splits<T, 64>(B, H, N, causal, n_splits);
+    case 96: return suggest_splits<T, 96>(B, H, N, causal, n_splits);
     case 128: return suggest_splits<T, 128>(B, H, N, causal, n_splits);
     default:
       if constexpr (sizeof(T) == 2) return suggest_splits<T, 256>(B, H, N, causal, n_splits);
@@ -189,7 +193,7 @@ int64_t part_o_bytes(int64_t S, int64_t BHN, int64_t D) { return ((S * BHN * D *
 int64_t split_workspace(int64_t S, int64_t BHN, int64_t D) { return part_o_bytes(S, BHN, D) + S * BHN * 4; }
 
 bool supported(int dtype, int64_t D) {
-  if (D == 32 || D == 64 || D == 128) return true;
+  if (D == 32 || D == 64 || D == 96 || D == 128) return true;
   return D == 256 && dtype != FA_F32;
 }
 
@@ -227,7 +231,7 @@ extern "C" const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid sizes (negative, or too large for the kernel's indexing)";
-    case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (forward: f32, bf16, f16 with D 32, 64, 128, and 256 for bf16/f16; backward: bf16, f16 with D 32, 64, 128)";
+    case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (forward: f32, bf16, f16 with D 32, 64, 96, 128, and 256 for bf16/f16; backward: bf16, f16 with D 32, 64, 96, 128)";
     case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE and kv_len 4 bytes)";
     case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
@@ -309,7 +313,7 @@ constexpr int kBwdWaves = 4;   // 128 query rows (dQ kernel) or 128 keys (dK/dV 
 constexpr int kBwdKeyTile = 64;
 
 bool bwd_supported(int dtype, int64_t D) {
-  return (dtype == FA_BF16 || dtype == FA_F16) && (D == 32 || D == 64 || D == 128);
+  return (dtype == FA_BF16 || dtype == FA_F16) && (D == 32 || D == 64 || D == 96 || D == 128);
 }
 
 int64_t bwd_stats_bytes(int64_t BH, int64_t N) {
@@ -335,8 +339,8 @@ int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipSt
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>),
                                  dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
-  if constexpr (D == 128) {
-    // K/V in LDS, eight waves (two per key group): two waves per SIMD at this head dimension.
+  if constexpr (D >= 96) {
+    // K/V in LDS, eight waves (two per key group): two waves per SIMD at these head dimensions.
     e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>),
                         dim3((unsigned)units), dim3(64 * 8), args, 0, stream);
   } else {
@@ -351,6 +355,7 @@ int dispatch_bwd(int64_t D, const fa::BwdParams& p, int64_t B, int64_t H, int64_
   switch (D) {
     case 32: return launch_bwd<T, 32>(p, B, H, N, s);
     case 64: return launch_bwd<T, 64>(p, B, H, N, s);
+    case 96: return launch_bwd<T, 96>(p, B, H, N, s);
     default: return launch_bwd<T, 128>(p, B, H, N, s);
   }
 }
@@ -562,7 +567,7 @@ extern "C" int fa_merge_states(const float* part_o, const float* part_lse, int n
                                void* stream) {
   if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
-  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 96 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   if (n_states < 1 || n_states > kMaxSplits) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) return FA_OK;
   const int64_t lim = INT64_MAX / 1024;

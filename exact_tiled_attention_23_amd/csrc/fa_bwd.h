@@ -93,22 +93,29 @@ __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh)
 // Per-lane copy plan of a [rows][D] tile into LDS, 1 KB per copy instruction: copy i of this
 // wave fills LDS rows (wave*LPW + i)*RPB + lane/CPR, physical chunk lane%CPR. In global memory
 // the rows are `stride` bytes apart (the token stride; below 2^31 / ROWS, checked by the host).
+// Rows of D = 96 are padded to the LDS row of D = 128 (lds_cols); a lane whose slot is a padding
+// chunk copies nothing.
 template <int D, int ROWS, int NW>
 struct TilePlan {
-  static constexpr int ROWB = D * 2;
-  static constexpr int CPR = D / 8;
+  static constexpr int DL = lds_cols<D>();
+  static constexpr bool PADDED = DL != D;
+  static constexpr int ROWB = DL * 2;
+  static constexpr int CPR = DL / 8;
   static constexpr int TILEB = ROWS * ROWB;
   static constexpr int LPW = TILEB / 1024 / NW;
   static constexpr int RPB = 1024 / ROWB;
   static_assert(TILEB % (1024 * NW) == 0, "tile must split evenly over waves");
   int row[LPW];
   unsigned chunk[LPW];  // byte offset, within the row, of the logical chunk this lane copies
+  bool data[LPW];       // that chunk holds data (not padding)
   __device__ __forceinline__ TilePlan(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int j = (wave * LPW + i) * RPB + lane / CPR;
+      const int lc = (lane % CPR) ^ swz_u<DL>(j);
       row[i] = j;
-      chunk[i] = ((lane % CPR) ^ swz_u<D>(j)) * 16;
+      chunk[i] = lc * 16;
+      data[i] = lc < D / 8;
     }
   }
   // Copy rows [r0, r0 + ROWS) of the tensor at `src` (n rows, `stride` bytes apart) into `dst`;
@@ -119,7 +126,7 @@ struct TilePlan {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int rr = min(row[i], n - 1 - r0);
-      lds_copy16(t, (unsigned)rr * stride + chunk[i], dst + (wave * LPW + i) * 1024);
+      if (!PADDED || data[i]) lds_copy16(t, (unsigned)rr * stride + chunk[i], dst + (wave * LPW + i) * 1024);
     }
   }
   // Zero this lane's slots of rows at or past `lim` (tile-relative).
@@ -134,7 +141,8 @@ struct TilePlan {
 // reduction chunk 2s + g.
 template <typename T, int D>
 __device__ __forceinline__ typename Mma<T>::frag row_frag(const unsigned char* t, int row, int chunk) {
-  return *reinterpret_cast<const typename Mma<T>::frag*>(t + row * (2 * D) + ((chunk ^ swz_u<D>(row)) * 16));
+  constexpr int DL = lds_cols<D>();
+  return *reinterpret_cast<const typename Mma<T>::frag*>(t + row * (2 * DL) + ((chunk ^ swz_u<DL>(row)) * 16));
 }
 
 // Transpose fragment: A operand whose rows are the head dimension (32 of them, block dt) and
@@ -144,8 +152,9 @@ __device__ __forceinline__ typename Mma<T>::frag tr_frag(const unsigned char* t,
   const int g = lane >> 5, s16 = lane & 15, s4 = s16 >> 2, sm = s16 & 3, q2 = (lane >> 4) & 1;
   const int c = 4 * dt + 2 * q2 + (sm >> 1);
   const int ra = row0 + 8 * g + s4, rb = ra + 4;
-  const unsigned char* pa = t + ra * (2 * D) + ((c ^ swz_u<D>(ra)) * 16) + (sm & 1) * 8;
-  const unsigned char* pb = t + rb * (2 * D) + ((c ^ swz_u<D>(rb)) * 16) + (sm & 1) * 8;
+  constexpr int DL = lds_cols<D>();
+  const unsigned char* pa = t + ra * (2 * DL) + ((c ^ swz_u<DL>(ra)) * 16) + (sm & 1) * 8;
+  const unsigned char* pb = t + rb * (2 * DL) + ((c ^ swz_u<DL>(rb)) * 16) + (sm & 1) * 8;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pb));
   return __builtin_bit_cast(typename Mma<T>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));

@@ -95,17 +95,25 @@ template <int D> __device__ __forceinline__ int swz_v(int j) {
   else return 0;  // D = 32: four consecutive rows already sit in four different bank quarters
 }
 
+// LDS row width, in elements, of a tile of head dimension D. Rows of D = 96 (192 bytes) do not
+// tile the 1 KB copy blocks, so they take the 256-byte row of D = 128 and its swizzles; their
+// last four 16-byte chunks are never copied nor read.
+template <int D> constexpr int lds_cols() { return D == 96 ? 128 : D; }
+
 template <typename T, int D, int BC, int NW, int WPE, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   static_assert(sizeof(T) == 2, "16-bit element types only");
-  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dimension");
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dimension");
   static_assert(BC % 32 == 0, "key tile");
   constexpr int BR = 32 * NW;
-  constexpr int ROWB = D * 2;                   // bytes per K/V row
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int DL = lds_cols<D>();
+  constexpr bool PADDED = DL != D;
+  constexpr int ROWB = DL * 2;                  // bytes per K/V row in LDS
+  constexpr int CPR = DL / 8;                   // 16-byte chunks per LDS row
+  constexpr int VCH = D / 8;                    // chunks of a row that hold data
   constexpr int TILEB = BC * ROWB;              // bytes per K (or V) tile
   constexpr int BLOCKS = TILEB / 1024;          // 1 KB global_load_lds blocks per tile
   constexpr int LPW = BLOCKS / NW;              // blocks per wave per tile (each for K and V)
@@ -165,15 +173,20 @@ void fwd16_kernel(FwdParams p) {
   // ---- per-lane constants of the global -> LDS copies: block blk = wave*LPW + i holds
   // rows blk*RPB .. +RPB-1; this lane fills the block's 16-byte slot `lane`, i.e. physical
   // chunk lane % CPR of row blk*RPB + lane / CPR, holding the logical chunk XOR swizzle.
+  // With padded rows, a lane whose slot holds a padding chunk copies nothing (ld_kok/ld_vok).
   int ld_row[LPW];
   unsigned ld_kb[LPW], ld_vb[LPW];  // byte offsets within a tile
+  bool ld_kok[LPW], ld_vok[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int j = (wave * LPW + i) * RPB + lane / CPR;
     const int pc = lane % CPR;
+    const int ck = pc ^ swz_k<DL>(j), cv = pc ^ swz_v<DL>(j);
     ld_row[i] = j;
-    ld_kb[i] = j * ksnb + (pc ^ swz_k<D>(j)) * 16;
-    ld_vb[i] = j * vsnb + (pc ^ swz_v<D>(j)) * 16;
+    ld_kb[i] = j * ksnb + ck * 16;
+    ld_vb[i] = j * vsnb + cv * 16;
+    ld_kok[i] = ck < VCH;
+    ld_vok[i] = cv < VCH;
   }
 
   auto issue_tile = [&](int j0, int buf) {
@@ -186,8 +199,8 @@ void fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = wave * LPW + i;
-        lds_copy16(kt, ld_kb[i], kl + blk * 1024);
-        lds_copy16(vt, ld_vb[i], vl + blk * 1024);
+        if (!PADDED || ld_kok[i]) lds_copy16(kt, ld_kb[i], kl + blk * 1024);
+        if (!PADDED || ld_vok[i]) lds_copy16(vt, ld_vb[i], vl + blk * 1024);
       }
     } else {
       // Rows past the tensor end read row n-1 instead (their scores are masked and their
@@ -197,8 +210,8 @@ void fwd16_kernel(FwdParams p) {
         const int blk = wave * LPW + i;
         const int over = j0 + ld_row[i] - (n - 1);
         const unsigned rows_back = over > 0 ? (unsigned)over : 0u;
-        lds_copy16(kt, ld_kb[i] - rows_back * ksnb, kl + blk * 1024);
-        lds_copy16(vt, ld_vb[i] - rows_back * vsnb, vl + blk * 1024);
+        if (!PADDED || ld_kok[i]) lds_copy16(kt, ld_kb[i] - rows_back * ksnb, kl + blk * 1024);
+        if (!PADDED || ld_vok[i]) lds_copy16(vt, ld_vb[i] - rows_back * vsnb, vl + blk * 1024);
       }
     }
   };
@@ -219,13 +232,13 @@ void fwd16_kernel(FwdParams p) {
   const int kr = a_row_key<8>(r);                 // K row this lane feeds as A-operand row r
   int koff[NQF];
 #pragma unroll
-  for (int s = 0; s < NQF; ++s) koff[s] = kr * ROWB + ((2 * s + g) ^ swz_k<D>(kr)) * 16;
+  for (int s = 0; s < NQF; ++s) koff[s] = kr * ROWB + ((2 * s + g) ^ swz_k<DL>(kr)) * 16;
   const int s16 = lane & 15, s4 = s16 >> 2, sm = s16 & 3, q2 = (lane >> 4) & 1;
   int voff[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     const int c = 4 * dt + 2 * q2 + (sm >> 1);
-    voff[dt] = (8 * g + s4) * ROWB + ((c ^ swz_v<D>(s4)) * 16) + (sm & 1) * 8;
+    voff[dt] = (8 * g + s4) * ROWB + ((c ^ swz_v<DL>(s4)) * 16) + (sm & 1) * 8;
   }
 
   f32x16 oacc[NDT];

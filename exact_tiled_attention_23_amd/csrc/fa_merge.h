@@ -12,7 +12,7 @@
 //
 // Memory-bound: each row reads S*(D+1) floats and writes D elements and one float.
 // Threads take 4 consecutive columns of one row (16-byte loads); a 256-thread block
-// covers 256 / (D/4) rows.
+// covers floor(256 / (D/4)) rows (10 at D = 96, whose last 16 threads stay idle).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int RPB = 256 / TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 4;
-  if (row >= p.rows) return;
+  if (threadIdx.x >= RPB * TPR || row >= p.rows) return;
   float m = -INFINITY;
   for (int s = 0; s < p.n_states; ++s) m = fmaxf(m, p.part_lse[s * p.rows + row]);
   float4 acc = {0.f, 0.f, 0.f, 0.f};

@@ -56,7 +56,7 @@ enum {
  * LSE     : device pointer, contiguous [B][H][N] float32 (fully overwritten):
  *           ln of the softmax denominator in units of scaled logits; -inf for a
  *           fully masked row.
- * B, H, N, D : sizes. D must be 32, 64 or 128 (or 256 for bf16/f16). If any of B, H,
+ * B, H, N, D : sizes. D must be 32, 64, 96 or 128 (or 256 for bf16/f16). If any of B, H,
  *           N is 0 the call does nothing and returns FA_OK (pointers are then not inspected).
  * scale   : softmax scale applied to Q.K^T; finite and > 0 (1/sqrt(D) is usual).
  * causal  : 1 for the causal mask, 0 for none.
@@ -88,7 +88,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *           Q, K and V may overlap themselves (a stride of 0 shares one K/V head among all
  *           query heads); O must not (no two (b, h, n, d) may name the same element).
  *           K and V token strides may not exceed 16 MiB. LSE stays contiguous [B][H][N].
- * D       : 32, 64 or 128 for every dtype; 256 for FA_BF16 and FA_F16.
+ * D       : 32, 64, 96 or 128 for every dtype; 256 for FA_BF16 and FA_F16.
  * Other arguments, ownership and errors as fa_fwd; a negative stride or an overlapping O
  * gives FA_ERR_ARG, a misaligned stride FA_ERR_ALIGN.
  */
@@ -160,7 +160,7 @@ int fa_fwd_split_count(int64_t B, int64_t H, int64_t N, int64_t D, int causal, i
  * O        : device pointer of `dtype`, strided as o_strides (3 int64 element strides
  *            {b, h, n} on the host, or NULL for contiguous [B][H][N][D]); fully overwritten.
  * LSE      : device pointer, contiguous float32 [B][H][N]; fully overwritten.
- * D        : 32, 64, 128 or 256 for every dtype.
+ * D        : 32, 64, 96, 128 or 256 for every dtype.
  * One kernel on `stream`; nothing is allocated. Errors as fa_fwd_strided, FA_ERR_ARG for
  * n_states out of range.
  */
@@ -196,7 +196,7 @@ int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
  * LSE     : device pointer, contiguous [B][H][N] float32 (read only).
  * dQ, dK, dV : device pointers, contiguous [B][H][N][D] of `dtype` (fully overwritten); they may
  *           not overlap each other, any input, or the workspace.
- * D       : 32, 64 or 128. dtype: FA_BF16 or FA_F16 (FA_F32 gives FA_ERR_UNSUPPORTED).
+ * D       : 32, 64, 96 or 128. dtype: FA_BF16 or FA_F16 (FA_F32 gives FA_ERR_UNSUPPORTED).
  * workspace, workspace_bytes : device memory of at least fa_bwd_workspace_bytes(B, H, N, D)
  *           bytes, 256-byte aligned; its contents on entry do not matter.
  * Arithmetic: the products run on the matrix cores with float32 accumulation; P and dS are

@@ -118,7 +118,7 @@ SWEEP_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 200, 300]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_sweep(dtype, D, causal):
     """Ragged N around the 64-row and 128-row tile edges; B=2, H=2."""
@@ -130,17 +130,18 @@ def test_backward_sweep(dtype, D, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 96])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_key_padding(dtype, causal):
+def test_backward_key_padding(dtype, D, causal):
     """kv_len 0 (all gradients 0), 1, a tile edge, ragged, N; padded keys hold NaN."""
-    N, D = 333, 64
+    N = 333
     kv = np.array([0, 1, 128, 201, N], dtype=np.int32)
     x = generate(5, 2, N, D, dtype, causal=causal, seed=81)
     for b, L in enumerate(kv):       # padding keys may hold anything: NaN must not leak
         x.k[b, :, L:] = float("nan")
         x.v[b, :, L:] = float("nan")
     do = generate_grad_output(5, 2, N, D, dtype, seed=82)
-    say(f"bwd padding dtype={dtype} causal={causal}")
+    say(f"bwd padding dtype={dtype} D={D} causal={causal}")
     got = run_bwd(x, do, kv_len=kv)
     xk = x.k.clone()
     xv = x.v.clone()
@@ -214,11 +215,12 @@ def test_backward_full_size_sampled():
                 compare_grad(gg[b:b + 1, h:h + 1], rr, tt, "bf16", f"full {name} b={b} h={h}")
 
 
-def test_backward_strided_layouts():
+@pytest.mark.parametrize("D", [96, 128])
+def test_backward_strided_layouts(D):
     """[B, N, H, D] storage seen as [B, H, N, D] for every input, dQ/dK/dV written into one packed
     [B, N, 3, H, D] tensor: bit-identical to the contiguous call (strides change addressing only),
     and within the bound of the oracle."""
-    B, H, N, D = 2, 3, 333, 128
+    B, H, N = 2, 3, 333
     x = generate(B, H, N, D, "bf16", causal=True, seed=401)
     do = generate_grad_output(B, H, N, D, "bf16", seed=402)
     q, k, v, dO = (t.to(DEV) for t in (x.q, x.k, x.v, do))
@@ -228,7 +230,7 @@ def test_backward_strided_layouts():
     qs, ks, vs, os_, dos = (bnhd(t) for t in (q, k, v, o, dO))
     packed = torch.full((B, N, 3, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
     dq, dk, dv = (packed[:, :, i].transpose(1, 2) for i in range(3))
-    say("bwd strided: BNHD inputs, packed outputs")
+    say(f"bwd strided D={D}: BNHD inputs, packed outputs")
     fa.backward(qs, ks, vs, os_, lse, dos, causal=True, scale=x.scale, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     for a, b_, name in zip((dq, dk, dv), ref_grads, ("dQ", "dK", "dV")):
@@ -240,7 +242,7 @@ def test_backward_strided_layouts():
         compare_grad(g, r, t, "bf16", f"strided {name}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 96, 128])
 def test_backward_shared_kv_head(D):
     """One K/V head shared by every query head (zero head stride): dK and dV come out per query
     head and equal the gradients of attention with that K/V repeated in every head."""

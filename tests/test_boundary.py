@@ -56,9 +56,20 @@ def test_negative_sizes(field):
     assert call(**{field: -1}) == binding.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("D", [0, 16, 48, 96, 100, 512])
+@pytest.mark.parametrize("D", [0, 16, 48, 80, 100, 112, 512])
 def test_unsupported_head_dim(D):
     assert call(D=D) == binding.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", [fa.FA_F32, fa.FA_BF16, fa.FA_F16])
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+def test_supported_head_dims_pass_the_checks(D, dtype):
+    # N = 0: every check up to the empty-call no-op runs, and nothing is launched.
+    assert call(D=D, N=0, dtype=dtype) == binding.FA_OK
+    assert call_split(D=D, N=0, dtype=dtype) == binding.FA_OK
+    assert call_merge(D=D, N=0, dtype=dtype) == binding.FA_OK
+    want = binding.FA_ERR_UNSUPPORTED if dtype == fa.FA_F32 else binding.FA_OK
+    assert call_bwd(D=D, N=0, dtype=dtype) == want
 
 
 def test_head_dim_256_is_16_bit_only():
@@ -228,7 +239,7 @@ def test_split_workspace_checks():
 
 def test_split_shares_forward_validation():
     assert call_split(B=-1) == binding.FA_ERR_SHAPE
-    assert call_split(D=96) == binding.FA_ERR_UNSUPPORTED
+    assert call_split(D=80) == binding.FA_ERR_UNSUPPORTED
     assert call_split(scale=0.0) == binding.FA_ERR_ARG
     assert call_split(Q=0) == binding.FA_ERR_NULL
     assert call_split(O=A + 8) == binding.FA_ERR_ALIGN
@@ -249,7 +260,7 @@ def call_merge(n_states=2, o_strides=None, **kw):
 
 def test_merge_validation():
     assert call_merge(B=-1) == binding.FA_ERR_SHAPE
-    assert call_merge(D=96) == binding.FA_ERR_UNSUPPORTED
+    assert call_merge(D=80) == binding.FA_ERR_UNSUPPORTED
     assert call_merge(dtype=7) == binding.FA_ERR_UNSUPPORTED
     for S in (0, 257):
         assert call_merge(n_states=S) == binding.FA_ERR_ARG
@@ -272,7 +283,7 @@ def test_merge_empty_is_noop():
 
 def test_split_count_validation_and_empty():
     assert fa.fa_fwd_split_count(-1, 1, 8, 64, 1, fa.FA_BF16)[0] == binding.FA_ERR_SHAPE
-    assert fa.fa_fwd_split_count(1, 1, 8, 96, 1, fa.FA_BF16)[0] == binding.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_split_count(1, 1, 8, 80, 1, fa.FA_BF16)[0] == binding.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_split_count(1, 1, 8, 256, 1, fa.FA_F32)[0] == binding.FA_ERR_UNSUPPORTED
     assert fa.fa_fwd_split_count(1, 1, 8, 64, 2, fa.FA_BF16)[0] == binding.FA_ERR_ARG
     assert binding.load_library().fa_fwd_split_count(1, 1, 8, 64, 1, fa.FA_BF16, None) == binding.FA_ERR_NULL
@@ -311,7 +322,7 @@ def test_bwd_validation():
     assert call_bwd(B=-1) == binding.FA_ERR_SHAPE
     assert call_bwd(dtype=fa.FA_F32) == binding.FA_ERR_UNSUPPORTED
     assert call_bwd(dtype=9) == binding.FA_ERR_UNSUPPORTED
-    for D in (16, 96, 256):
+    for D in (16, 80, 256):
         assert call_bwd(D=D) == binding.FA_ERR_UNSUPPORTED
     assert call_bwd(scale=float("nan")) == binding.FA_ERR_ARG
     assert call_bwd(causal=3) == binding.FA_ERR_ARG

@@ -83,15 +83,21 @@ def test_small_sweep(dtype, D, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 96])
 @pytest.mark.parametrize("causal", [False, True])
-def test_key_padding(dtype, causal):
-    """Per-batch kv_len including 0, 1, a tile edge, a ragged value and N."""
-    N, D = 200, 64
+def test_key_padding(dtype, D, causal):
+    """Per-batch kv_len including 0, 1, a tile edge, a ragged value and N; the padding keys
+    hold NaN, which must not reach O or LSE."""
+    N = 200
     kv = np.array([0, 1, 64, 131, 200], dtype=np.int32)
-    say(f"padding dtype={dtype} causal={causal} kv={kv.tolist()}")
+    say(f"padding dtype={dtype} D={D} causal={causal} kv={kv.tolist()}")
     x = generate(5, 2, N, D, dtype, causal=causal, seed=77)
+    k0, v0 = x.k.clone(), x.v.clone()
+    for b, L in enumerate(kv):
+        x.k[b, :, L:] = float("nan")
+        x.v[b, :, L:] = float("nan")
     o, lse = run_gpu(x, kv_len=kv)
-    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal, kv_len=kv)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(k0), to_f64(v0), x.scale, causal=causal, kv_len=kv)
     compare(o, lse, ro, rl, dtype, "padding")
     assert (o[0] == 0).all().item() and torch.isinf(lse[0]).all().item() and (lse[0] < 0).all().item()
 
@@ -229,11 +235,12 @@ def test_full_size_workload(name):
     assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
-# ---------------------------------------------------------------- head dimensions 32 and 256
-@pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 32), ("f16", 32), ("bf16", 256), ("f16", 256)])
+# ---------------------------------------------------------------- head dimensions 32, 96 and 256
+@pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 32), ("f16", 32), ("f32", 96), ("bf16", 96), ("f16", 96),
+                                     ("bf16", 256), ("f16", 256)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_other_head_dims(dtype, D, causal):
-    """Ragged N around the tile edges for D = 32 and D = 256, with and without padding."""
+    """Ragged N around the tile edges for D = 32, 96 and 256, with and without padding."""
     for N in (1, 17, 64, 129, 300):
         say(f"head dim dtype={dtype} D={D} causal={causal} N={N}")
         x = generate(3, 2, N, D, dtype, causal=causal, seed=2000 + N + D)
@@ -252,7 +259,7 @@ def _strided_run(x, q, k, v, out, causal, kv=None):
     return o, lse
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 64), ("bf16", 256)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64), ("f32", 64), ("bf16", 96), ("f32", 96), ("bf16", 256)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bnhd_layout(dtype, D, causal):
     """[B, N, H, D] storage seen as [B, H, N, D] (token stride H*D, head stride D), for

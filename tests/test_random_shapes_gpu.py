@@ -27,7 +27,7 @@ def draw_configs(count=30, seed=2024):
     out = []
     for i in range(count):
         dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
-        D = int(rng.choice([32, 64, 128] + ([] if dtype == "f32" else [256])))
+        D = int(rng.choice([32, 64, 96, 128] + ([] if dtype == "f32" else [256])))
         B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         N = int(rng.integers(1, 701))
         causal = bool(rng.integers(0, 2))

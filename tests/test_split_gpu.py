@@ -69,7 +69,7 @@ def test_split_key_padding(dtype, causal):
         assert (o[0] == 0).all().item() and torch.isinf(lse[0]).all().item()
 
 
-@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("D", [32, 96, 256])
 def test_split_other_head_dims(D):
     for causal in (False, True):
         say(f"split D={D} causal={causal}")
@@ -177,7 +177,7 @@ def oracle_parts(x, bounds):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("D", [32, 64, 128, 256])
+@pytest.mark.parametrize("D", [32, 64, 96, 128, 256])
 def test_merge_states_matches_oracle(dtype, D):
     N = 190
     x = generate(2, 2, N, D, "f32", causal=False, seed=4000 + D)
