@@ -235,6 +235,25 @@ def test_full_size_workload(name):
     assert torch.equal(o, o2) and torch.equal(lse, l2)
 
 
+# ---------------------------------------------------------------- workgroup shape by problem size
+@pytest.mark.parametrize("D", [96, 128])
+@pytest.mark.parametrize("N", [1792, 2048])
+def test_causal_workgroup_shape_threshold(D, N):
+    """Causal D = 96 / 128 problems run 4-wave workgroups below 2048 tiles of 256 query rows
+    and 8-wave ones from there on: B=16 H=16 gives 1792 and 2048 such tiles. Sampled rows
+    of a few heads against the oracle, on both sides of the threshold."""
+    B, H = 16, 16
+    say(f"workgroup-shape threshold D={D} N={N} ({B * H * ((N + 255) // 256)} tiles of 256 rows)")
+    x = generate(B, H, N, D, "bf16", causal=True, seed=4100 + N + D)
+    o, lse = run_gpu(x)
+    ocpu, lcpu = o.float().cpu(), lse.cpu()
+    rows = np.array([0, 1, 127, 128, 255, 256, 1000, N - 129, N - 128, N - 1])
+    for b, h in [(0, 0), (7, 9), (15, 15)]:
+        ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
+                                  to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=True, rows=rows)
+        compare(ocpu[b:b + 1, h:h + 1, rows], lcpu[b:b + 1, h:h + 1, rows], ro, rl, "bf16", f"D={D} N={N} b={b} h={h}")
+
+
 # ---------------------------------------------------------------- head dimensions 32, 96 and 256
 @pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 32), ("f16", 32), ("f32", 96), ("bf16", 96), ("f16", 96),
                                      ("bf16", 256), ("f16", 256)])
