@@ -24,6 +24,12 @@ can be rebuilt later, and the backward uses them for dQ, dK, dV). It never
 holds a full row of P: it rebuilds each block P_ij = exp(S_ij - LSE_i) from the
 saved LSE, and uses Delta_i = rowsum(dO_i o O_i) in place of rowsum(P o dP).
 A row with no valid key (LSE = -inf) gets P = 0: its output is the constant 0.
+
+With query padding (q_len), a row at or past q_len[b] is not part of the batch element: its
+output is the constant 0 and its rows of Q and dO are not inputs at all, so they are replaced
+by zeros before the definition is applied. That alone gives the padding rows dP = dO V^T = 0,
+hence dS = P o (0 - 0) = 0: their dQ rows are exactly 0 and they add nothing to dK or dV,
+whatever Q and dO held there (NaN included).
 """
 
 import numpy as np
@@ -37,6 +43,18 @@ def _valid_mask(n_rows, n_keys, causal, kv_len_b, rows=None):
     if causal:
         valid &= keys[None, :] <= pos[:, None]
     return valid
+
+
+def _drop_padding_queries(x, q_len, rows=None):
+    """Copy of x [B, H, R, ...] with the rows of padding queries (position >= q_len[b]) zeroed."""
+    if q_len is None:
+        return x
+    x = x.copy()
+    q_len = np.asarray(q_len).reshape(-1)
+    pos = np.arange(x.shape[2]) if rows is None else np.asarray(rows)
+    for b in range(x.shape[0]):
+        x[b, :, pos >= int(q_len[b])] = 0.0
+    return x
 
 
 def _probs_and_ds(q, k, v, do, scale, valid):
@@ -63,11 +81,12 @@ def _grad_one_head(q, k, v, do, scale, valid):
     return dq, dk, dv
 
 
-def attention_grad(q, k, v, do, scale, causal=False, kv_len=None):
+def attention_grad(q, k, v, do, scale, causal=False, kv_len=None, q_len=None):
     """Gradients (dq, dk, dv) of sum(dO o O) for exact attention, by the definition.
 
     q, k: [B, H, N, D]; v, do: [B, H, N, Dv]; kv_len: None or ints [B] (keys at or past
-    kv_len[b] are padding). Returns float64 arrays shaped like q, k, v.
+    kv_len[b] are padding); q_len: None or ints [B] (query rows at or past q_len[b] are
+    padding). Returns float64 arrays shaped like q, k, v.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -76,6 +95,8 @@ def attention_grad(q, k, v, do, scale, causal=False, kv_len=None):
     B, H, N, D = q.shape
     if k.shape != (B, H, N, D) or v.shape[:3] != (B, H, N) or do.shape != v.shape:
         raise ValueError("q, k, v, do shapes disagree")
+    q = _drop_padding_queries(q, q_len)
+    do = _drop_padding_queries(do, q_len)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -87,7 +108,7 @@ def attention_grad(q, k, v, do, scale, causal=False, kv_len=None):
     return dq, dk, dv
 
 
-def attention_grad_rows(q, k, v, do, scale, rows, causal=False, kv_len=None):
+def attention_grad_rows(q, k, v, do, scale, rows, causal=False, kv_len=None, q_len=None):
     """dQ for the selected query positions only, [B, H, len(rows), D]: each dQ row depends on
     its own query row and every key, so sampled rows cost O(len(rows) * N * D)."""
     q = np.asarray(q, dtype=np.float64)
@@ -96,6 +117,8 @@ def attention_grad_rows(q, k, v, do, scale, rows, causal=False, kv_len=None):
     do = np.asarray(do, dtype=np.float64)
     B, H, N, D = q.shape
     rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    q = _drop_padding_queries(q, q_len)
+    do = _drop_padding_queries(do, q_len)
     out = np.zeros((B, H, rows.size, D))
     for b in range(B):
         L = N if kv_len is None else int(np.asarray(kv_len).reshape(-1)[b])

@@ -11,6 +11,9 @@ hardened masking for padding and empty rows):
 
   * the valid keys of row i are J_i = { j : j < kv_len[b] and (not causal
     or j <= i) }, a prefix [0, count_i) of the key axis;
+  * a query row at or past q_len[b] is padding: it is not part of the batch
+    element, so it has no valid keys (J_i empty) whatever Q holds there
+    (the pages' hardened masking for padding, applied to the query side);
   * if J_i is empty the row is fully masked: O = 0 and LSE = -inf
     ("js-flash-attention-tiled-online-softmax-exactness", Root causes
     addressed 2 and Verification: fully masked rows give finite zeros);
@@ -27,12 +30,15 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 
-def key_counts(positions, n_keys, causal, kv_len_b):
-    """Number of valid keys of each query position (the length of the prefix J_i)."""
+def key_counts(positions, n_keys, causal, kv_len_b, q_len_b=None):
+    """Number of valid keys of each query position (the length of the prefix J_i); 0 for a
+    padding query (position >= q_len_b)."""
     positions = np.asarray(positions, dtype=np.int64)
     counts = np.full(positions.shape, min(int(kv_len_b), int(n_keys)), dtype=np.int64)
     if causal:
         counts = np.minimum(counts, positions + 1)
+    if q_len_b is not None:
+        counts = np.where(positions < int(q_len_b), counts, 0)
     return np.maximum(counts, 0)
 
 
@@ -60,7 +66,7 @@ def _rows_of_one_head(q, k, v, scale, counts):
     return o, lse
 
 
-def attention(q, k, v, scale, causal=False, kv_len=None, rows=None, row_chunk=512, workers=1):
+def attention(q, k, v, scale, causal=False, kv_len=None, rows=None, row_chunk=512, workers=1, q_len=None):
     """Exact attention by the definition, in float64.
 
     Parameters
@@ -69,6 +75,8 @@ def attention(q, k, v, scale, causal=False, kv_len=None, rows=None, row_chunk=51
     scale : the softmax scale, as the exact number the caller's other path uses.
     causal : hide keys j > i from query i.
     kv_len : None (every key valid) or ints [B]; keys j >= kv_len[b] are padding.
+    q_len : None (every query present) or ints [B]; query rows i >= q_len[b] are
+        padding and come out as O = 0, LSE = -inf.
     rows : None for every query position, or a 1-D array of query positions;
         then only those rows are computed, for every (b, h).
     row_chunk : query rows per matrix product (bounds memory).
@@ -90,6 +98,10 @@ def attention(q, k, v, scale, causal=False, kv_len=None, rows=None, row_chunk=51
         kv_len = np.asarray(kv_len).reshape(-1)
         if kv_len.shape != (B,):
             raise ValueError("kv_len must have one entry per batch")
+    if q_len is not None:
+        q_len = np.asarray(q_len).reshape(-1)
+        if q_len.shape != (B,):
+            raise ValueError("q_len must have one entry per batch")
     R = positions.size
     o = np.zeros((B, H, R, v.shape[3]))
     lse = np.empty((B, H, R))
@@ -97,9 +109,10 @@ def attention(q, k, v, scale, causal=False, kv_len=None, rows=None, row_chunk=51
     def one_head(bh):
         b, h = divmod(bh, H)
         L = N if kv_len is None else int(kv_len[b])
+        Lq = None if q_len is None else int(q_len[b])
         for c0 in range(0, R, row_chunk):
             pos = positions[c0:c0 + row_chunk]
-            counts = key_counts(pos, N, causal, L)
+            counts = key_counts(pos, N, causal, L, Lq)
             o[b, h, c0:c0 + pos.size], lse[b, h, c0:c0 + pos.size] = _rows_of_one_head(
                 q[b, h, pos], k[b, h], v[b, h], float(scale), counts)
 

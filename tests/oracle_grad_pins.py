@@ -26,12 +26,12 @@ def _inputs(seed, B, H, N, D, Dv=None, scale_q=1.0):
     return q, k, v, do
 
 
-def _loss(q, k, v, do, scale, causal, kv_len):
-    o, _ = oracle.attention(q, k, v, scale, causal=causal, kv_len=kv_len)
+def _loss(q, k, v, do, scale, causal, kv_len, q_len=None):
+    o, _ = oracle.attention(q, k, v, scale, causal=causal, kv_len=kv_len, q_len=q_len)
     return float((o * do).sum())
 
 
-def finite_difference(q, k, v, do, scale, causal, kv_len, h=1e-6):
+def finite_difference(q, k, v, do, scale, causal, kv_len, h=1e-6, q_len=None):
     """Central differences of sum(dO o O) through the forward oracle, one element at a time."""
     grads = []
     args = [q.copy(), k.copy(), v.copy()]
@@ -40,9 +40,9 @@ def finite_difference(q, k, v, do, scale, causal, kv_len, h=1e-6):
         for idx in np.ndindex(*args[t].shape):
             keep = args[t][idx]
             args[t][idx] = keep + h
-            up = _loss(*args, do, scale, causal, kv_len)
+            up = _loss(*args, do, scale, causal, kv_len, q_len)
             args[t][idx] = keep - h
-            dn = _loss(*args, do, scale, causal, kv_len)
+            dn = _loss(*args, do, scale, causal, kv_len, q_len)
             args[t][idx] = keep
             g[idx] = (up - dn) / (2 * h)
         grads.append(g)
@@ -132,6 +132,30 @@ def pin_grad_special_cases(grad):
 
 
 ALL_GRAD_PINS = [pin_grad_finite_difference, pin_grad_torch_autograd, pin_grad_invariants, pin_grad_special_cases]
+
+
+def pin_grad_query_padding(grad):
+    """Query padding (q_len): every element of dQ, dK, dV against central differences of the
+    pinned forward with the same q_len (its padding rows are the constant 0, so their dO drops
+    out); NaN in the padding rows of Q and dO changes nothing, and their dQ rows are exactly 0."""
+    q, k, v, do = _inputs(46, 2, 2, 4, 3, Dv=2)
+    for causal in (False, True):
+        for kv in (None, np.array([3, 4])):
+            for ql in (np.array([2, 4]), np.array([0, 3])):
+                want = finite_difference(q, k, v, do, 0.7, causal, kv, q_len=ql)
+                got = grad(q, k, v, do, 0.7, causal=causal, kv_len=kv, q_len=ql)
+                tag = f"causal={causal} kv={kv} q_len={ql}"
+                for name, a, b in zip(("dQ", "dK", "dV"), got, want):
+                    _close(a, b, 1e-7, 1e-8, f"finite difference {name} " + tag)
+                qn, don = q.copy(), do.copy()
+                for b in range(2):
+                    qn[b, :, ql[b]:] = np.nan
+                    don[b, :, ql[b]:] = np.nan
+                got_nan = grad(qn, k, v, don, 0.7, causal=causal, kv_len=kv, q_len=ql)
+                for name, a, b in zip(("dQ", "dK", "dV"), got_nan, got):
+                    assert np.array_equal(a, b), f"NaN padding rows change {name} " + tag
+                for b in range(2):
+                    assert (got_nan[0][b, :, ql[b]:] == 0).all(), "padding dQ rows " + tag
 
 
 def failing_grad_pins(grad):

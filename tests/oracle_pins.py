@@ -260,6 +260,34 @@ ALL_PINS = [pin_brute_force_exhaustive, pin_brute_force_batched, pin_golden, pin
             pin_permutation, pin_convex]
 
 
+def pin_query_padding(attn):
+    """Query padding (q_len): rows are independent in the definition, so a row before q_len[b]
+    equals the unpadded result (to rounding: the matrix products run over fewer rows), a row at
+    or past it is exactly O = 0, LSE = -inf, q_len = N changes nothing, and NaN in the padding
+    rows of Q reaches nothing."""
+    rng = np.random.default_rng(61)
+    q, k, v = (rng.standard_normal((2, 2, 7, 3)) for _ in range(3))
+    for causal in (False, True):
+        for kv in (None, np.array([5, 2])):
+            o0, l0 = attn(q, k, v, 0.8, causal=causal, kv_len=kv)
+            o, l = attn(q, k, v, 0.8, causal=causal, kv_len=kv, q_len=np.array([7, 7]))
+            assert np.array_equal(o, o0) and np.array_equal(l, l0), "q_len = N"
+            for ql in (np.array([3, 0]), np.array([6, 1])):
+                qn = q.copy()
+                for b in range(2):
+                    qn[b, :, ql[b]:] = np.nan
+                for qq in (q, qn):
+                    with np.errstate(invalid="ignore"):
+                        o, l = attn(qq, k, v, 0.8, causal=causal, kv_len=kv, q_len=ql)
+                    for b in range(2):
+                        L = int(ql[b])
+                        tag = f"causal={causal} kv={kv} q_len={ql} b={b}"
+                        _close(o[b, :, :L], o0[b, :, :L], 1e-14, 1e-15, "rows before q_len " + tag)
+                        _close(l[b, :, :L], l0[b, :, :L], 1e-14, 1e-15, "LSE before q_len " + tag)
+                        assert (o[b, :, L:] == 0).all(), "padding rows O " + tag
+                        assert (np.isneginf(l[b, :, L:])).all(), "padding rows LSE " + tag
+
+
 def failing_pins(attn):
     """Names of the pins that ``attn`` breaks (an exception of any kind counts as broken)."""
     bad = []

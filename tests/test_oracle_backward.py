@@ -96,6 +96,30 @@ GRAD_MUTANTS = {
 }
 
 
+def test_grad_oracle_query_padding_pin():
+    from oracle_grad_pins import pin_grad_query_padding
+    pin_grad_query_padding(oracle.attention_grad)
+
+
+GRAD_QUERY_PADDING_MUTANTS = {
+    "padding-dO-kept": ("    q = _drop_padding_queries(q, q_len)\n    do = _drop_padding_queries(do, q_len)\n    dq = np.zeros_like(q)",
+                        "    q = _drop_padding_queries(q, q_len)\n    dq = np.zeros_like(q)"),
+    "padding-q-kept": ("    q = _drop_padding_queries(q, q_len)\n    do = _drop_padding_queries(do, q_len)\n    dq = np.zeros_like(q)",
+                       "    do = _drop_padding_queries(do, q_len)\n    dq = np.zeros_like(q)"),
+    "padding-off-by-one": ("        x[b, :, pos >= int(q_len[b])] = 0.0", "        x[b, :, pos > int(q_len[b])] = 0.0"),
+    "padding-rows-not-zeroed": ("        x[b, :, pos >= int(q_len[b])] = 0.0", "        pass"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GRAD_QUERY_PADDING_MUTANTS))
+def test_grad_query_padding_mutant_is_caught(name):
+    from oracle_grad_pins import pin_grad_query_padding
+    mod = _mutant(oracle.backward, *GRAD_QUERY_PADDING_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            pin_grad_query_padding(mod.attention_grad)
+
+
 @pytest.mark.parametrize("name", sorted(GRAD_MUTANTS))
 def test_grad_mutant_is_caught(name):
     mod = _mutant(oracle.backward, *GRAD_MUTANTS[name])

@@ -60,6 +60,29 @@ def test_unmutated_naive_passes_every_pin():
     assert failing_pins(oracle.attention) == []
 
 
+QUERY_PADDING_MUTANTS = {
+    "query-padding-off-by-one": ("counts = np.where(positions < int(q_len_b), counts, 0)",
+                                 "counts = np.where(positions <= int(q_len_b), counts, 0)"),
+    "query-padding-ignored": ("counts = np.where(positions < int(q_len_b), counts, 0)", "counts = counts"),
+    "query-padding-inverted": ("counts = np.where(positions < int(q_len_b), counts, 0)",
+                               "counts = np.where(positions < int(q_len_b), 0, counts)"),
+}
+
+
+def test_oracle_query_padding_pin():
+    from oracle_pins import pin_query_padding
+    pin_query_padding(oracle.attention)
+
+
+@pytest.mark.parametrize("name", sorted(QUERY_PADDING_MUTANTS))
+def test_query_padding_mutant_is_caught(name):
+    from oracle_pins import pin_query_padding
+    mod = _mutant(oracle.naive, *QUERY_PADDING_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            pin_query_padding(mod.attention)
+
+
 TILED_MUTANTS = {
     "no-rescale-l": ("l = correction * l + p.sum(axis=-1)", "l = l + p.sum(axis=-1)"),
     "no-rescale-acc": ("acc = correction[..., None] * acc + np.matmul(p, v[:, :, k0:k1])",
