@@ -39,15 +39,15 @@ def load_library():
         lib.fa_fwd_strided.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
-                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_int64
         lib.fa_fwd_split_workspace_bytes.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         lib.fa_fwd_split.restype = ctypes.c_int
         lib.fa_fwd_split.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
-                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_int64, ctypes.c_void_p]
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.fa_fwd_split_count.restype = ctypes.c_int
         lib.fa_fwd_split_count.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                                                   ctypes.POINTER(ctypes.c_int)]
@@ -63,8 +63,8 @@ def load_library():
             ctypes.c_void_p]
         lib.fa_bwd_strided.restype = ctypes.c_int
         lib.fa_bwd_strided.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
-            ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_int64, ctypes.c_void_p]
+            ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -78,10 +78,12 @@ def fa_fwd(Q, K, V, O, LSE, B, H, N, D, scale, causal, kv_len, dtype, stream):
     return load_library().fa_fwd(Q, K, V, O, LSE, B, H, N, D, scale, causal, kv_len, dtype, stream)
 
 
-def fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, stream):
-    """Raw C call with strides: None (contiguous) or 12 ints (q, k, v, o; batch, head, token)."""
+def fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, q_len, kv_len, dtype, stream):
+    """Raw C call with strides: None (contiguous) or 12 ints (q, k, v, o; batch, head, token);
+    q_len and kv_len device pointers (0 for NULL)."""
     arr = _int64_array(strides, 12, "strides")
-    return load_library().fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, kv_len, dtype, stream)
+    return load_library().fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, q_len, kv_len, dtype,
+                                         stream)
 
 
 def _int64_array(values, n, what):
@@ -97,12 +99,12 @@ def fa_fwd_split_workspace_bytes(B, H, N, D, n_splits):
     return load_library().fa_fwd_split_workspace_bytes(B, H, N, D, n_splits)
 
 
-def fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, n_splits, workspace,
+def fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, q_len, kv_len, dtype, n_splits, workspace,
                  workspace_bytes, stream):
     """Raw C call of the key-split forward; strides as fa_fwd_strided, workspace a device pointer."""
     arr = _int64_array(strides, 12, "strides")
-    return load_library().fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, kv_len, dtype, n_splits,
-                                       workspace, workspace_bytes, stream)
+    return load_library().fa_fwd_split(Q, K, V, O, LSE, B, H, N, D, arr, scale, causal, q_len, kv_len, dtype,
+                                       n_splits, workspace, workspace_bytes, stream)
 
 
 def fa_fwd_split_count(B, H, N, D, causal, dtype):
@@ -130,12 +132,12 @@ def fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, d
                                  workspace, workspace_bytes, stream)
 
 
-def fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, strides, scale, causal, kv_len, dtype, workspace,
-                   workspace_bytes, stream):
+def fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, strides, scale, causal, q_len, kv_len, dtype,
+                   workspace, workspace_bytes, stream):
     """Raw C call of the strided backward; strides None (contiguous) or 24 ints."""
     arr = _int64_array(strides, 24, "strides")
-    return load_library().fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, arr, scale, causal, kv_len,
-                                         dtype, workspace, workspace_bytes, stream)
+    return load_library().fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, arr, scale, causal, q_len,
+                                         kv_len, dtype, workspace, workspace_bytes, stream)
 
 
 def fa_strerror(code):
@@ -157,23 +159,28 @@ def _stream_handle(stream, dev):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _kv_len_device(kv_len, B, N, dev):
-    if kv_len is None:
+def _lengths_device(lens, B, N, dev, what):
+    """Per-batch lengths (kv_len or q_len) as a device int32 tensor [B], or None."""
+    if lens is None:
         return None
-    if isinstance(kv_len, torch.Tensor) and kv_len.is_cuda:
-        if kv_len.dtype != torch.int32 or kv_len.shape != (B,) or not kv_len.is_contiguous():
-            raise ValueError("device kv_len must be a contiguous int32 tensor [B]")
-        return kv_len
-    kv_cpu = torch.as_tensor(kv_len).to(torch.int64).reshape(-1)
-    if kv_cpu.shape != (B,):
-        raise ValueError("kv_len must have one entry per batch")
-    if B and (int(kv_cpu.min()) < 0 or int(kv_cpu.max()) > N):
-        raise ValueError("kv_len values must lie in [0, N]")
-    return kv_cpu.to(torch.int32).to(dev)
+    if isinstance(lens, torch.Tensor) and lens.is_cuda:
+        if lens.dtype != torch.int32 or lens.shape != (B,) or not lens.is_contiguous():
+            raise ValueError(f"device {what} must be a contiguous int32 tensor [B]")
+        return lens
+    cpu = torch.as_tensor(lens).to(torch.int64).reshape(-1)
+    if cpu.shape != (B,):
+        raise ValueError(f"{what} must have one entry per batch")
+    if B and (int(cpu.min()) < 0 or int(cpu.max()) > N):
+        raise ValueError(f"{what} values must lie in [0, N]")
+    return cpu.to(torch.int32).to(dev)
 
 
-def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None, stream=None, n_splits=1,
-            workspace=None):
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def forward(q, k, v, *, causal=True, scale=None, kv_len=None, q_len=None, out=None, lse=None, stream=None,
+            n_splits=1, workspace=None):
     """Attention forward on device tensors [B, H, N, D]. Returns (o, lse).
 
     q, k, v (and out) may be any strided views whose last dimension is contiguous,
@@ -184,6 +191,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
     pages' constructor options do. kv_len: None, or int32-convertible values
     per batch (a CPU sequence is range-checked here and copied to the device;
     a device int32 tensor is passed through and clamped to [0, N] by the kernel).
+    q_len: the same for the query side: rows at or past q_len[b] are padding, are not
+    read, and come out as O = 0, LSE = -inf.
 
     n_splits > 1 cuts every query tile's keys into that many parts processed by separate
     workgroups, then merges the partial states (fa_fwd_split); "auto" takes the count
@@ -212,12 +221,12 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, out=None, lse=None
         raise ValueError("out must be shaped and typed like q, with a contiguous head dimension")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
-    kv_dev = _kv_len_device(kv_len, B, N, dev)
-    kv_ptr = 0 if kv_dev is None else kv_dev.data_ptr()
+    kv_dev = _lengths_device(kv_len, B, N, dev, "kv_len")
+    q_dev = _lengths_device(q_len, B, N, dev, "q_len")
     handle = _stream_handle(stream, dev)
     strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, strides,
-            float(scale), 1 if causal else 0, kv_ptr, _TORCH_DTYPE[q.dtype])
+            float(scale), 1 if causal else 0, _ptr(q_dev), _ptr(kv_dev), _TORCH_DTYPE[q.dtype])
     with torch.cuda.device(dev):
         if n_splits == "auto":
             rc, n_splits = fa_fwd_split_count(B, H, N, D, 1 if causal else 0, _TORCH_DTYPE[q.dtype])
@@ -267,13 +276,14 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
     return out, lse
 
 
-def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=None, dk=None, dv=None,
+def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, q_len=None, dq=None, dk=None, dv=None,
              workspace=None, stream=None):
     """Gradients (dq, dk, dv) of the attention forward, from its outputs o and lse and the output
     gradient do. q, k, v, o, do, dq, dk, dv: device tensors [B, H, N, D] of one dtype (bfloat16 or
     float16), any strides with a contiguous last dimension (e.g. [B, N, H, D] storage transposed;
     a zero head stride on k and v shares one K/V head, and dk, dv are then per query head);
-    lse: contiguous float32 [B, H, N]. causal, scale and kv_len must be the forward's. workspace:
+    lse: contiguous float32 [B, H, N]. causal, scale, kv_len and q_len must be the forward's (rows at
+    or past q_len[b] are not read and get dq = 0). workspace:
     None (allocated here) or a device tensor of at least fa_bwd_workspace_bytes(B, H, N, D) bytes,
     256-byte aligned."""
     ts = (q, k, v, o, do)
@@ -302,13 +312,14 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, dq=No
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
-    kv_dev = _kv_len_device(kv_len, B, N, dev)
+    kv_dev = _lengths_device(kv_len, B, N, dev, "kv_len")
+    q_dev = _lengths_device(q_len, B, N, dev, "q_len")
     every = (q, k, v, o, do, dq, dk, dv)
     strides = None if all(t.is_contiguous() for t in every) else [x for t in every for x in t.stride()[:3]]
     with torch.cuda.device(dev):
         rc = fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, strides, float(scale),
-                            1 if causal else 0, 0 if kv_dev is None else kv_dev.data_ptr(), _TORCH_DTYPE[q.dtype],
+                            1 if causal else 0, _ptr(q_dev), _ptr(kv_dev), _TORCH_DTYPE[q.dtype],
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream_handle(stream, dev))
     _check(rc)
@@ -322,14 +333,15 @@ class FlashAttention:
     gradients from them. The tile size is fixed per head dimension by the kernels, and the
     statistics are always kept (the forward always returns LSE)."""
 
-    def __init__(self, causal=True, softmax_scale=None, kv_len=None):
+    def __init__(self, causal=True, softmax_scale=None, kv_len=None, q_len=None):
         self.causal = causal
         self.softmax_scale = softmax_scale
         self.kv_len = kv_len
+        self.q_len = q_len
         self._saved = None
 
     def forward(self, q, k, v):
-        o, lse = forward(q, k, v, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len)
+        o, lse = forward(q, k, v, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len, q_len=self.q_len)
         self._saved = (q, k, v, o, lse)
         return o
 
@@ -342,15 +354,16 @@ class FlashAttention:
         if self._saved is None:
             raise RuntimeError("backward() needs a forward() first")
         q, k, v, o, lse = self._saved
-        return backward(q, k, v, o, lse, do, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len)
+        return backward(q, k, v, o, lse, do, causal=self.causal, scale=self.softmax_scale, kv_len=self.kv_len,
+                        q_len=self.q_len)
 
 
 class _AttentionFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal, scale, kv_len):
-        o, lse = forward(q, k, v, causal=causal, scale=scale, kv_len=kv_len)
+    def forward(ctx, q, k, v, causal, scale, kv_len, q_len):
+        o, lse = forward(q, k, v, causal=causal, scale=scale, kv_len=kv_len, q_len=q_len)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.scale, ctx.kv_len = causal, scale, kv_len
+        ctx.causal, ctx.scale, ctx.kv_len, ctx.q_len = causal, scale, kv_len, q_len
         return o
 
     @staticmethod
@@ -358,12 +371,13 @@ class _AttentionFunction(torch.autograd.Function):
         q, k, v, o, lse = ctx.saved_tensors
         if do.stride(-1) != 1:
             do = do.contiguous()
-        dq, dk, dv = backward(q, k, v, o, lse, do, causal=ctx.causal, scale=ctx.scale, kv_len=ctx.kv_len)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = backward(q, k, v, o, lse, do, causal=ctx.causal, scale=ctx.scale, kv_len=ctx.kv_len,
+                              q_len=ctx.q_len)
+        return dq, dk, dv, None, None, None, None
 
 
-def attention(q, k, v, causal=True, scale=None, kv_len=None):
+def attention(q, k, v, causal=True, scale=None, kv_len=None, q_len=None):
     """Differentiable attention for torch autograd: forward() now, backward() (fa_bwd) when the
     graph is differentiated. q, k, v: bfloat16/float16 device tensors [B, H, N, D], D <= 128 for
     the backward; see forward() for the options."""
-    return _AttentionFunction.apply(q, k, v, causal, scale, kv_len)
+    return _AttentionFunction.apply(q, k, v, causal, scale, kv_len, q_len)

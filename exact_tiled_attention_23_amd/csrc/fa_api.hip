@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
 // bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
@@ -62,8 +62,8 @@ struct Split {
 
 template <typename T, int D, typename S>
 int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
-                 const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream,
-                 const Split& sp) {
+                 const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+                 hipStream_t stream, const Split& sp) {
   constexpr int NW = S::NW;
   constexpr int BR = 32 * NW;
   constexpr int threads = 64 * NW;
@@ -73,6 +73,7 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
   p.v = V;
   p.o = O;
   p.lse = LSE;
+  p.q_len = q_len;
   p.kv_len = kv_len;
   p.q_sb = st.q[0]; p.q_sh = st.q[1]; p.q_sn = st.q[2];
   p.k_sb = st.k[0]; p.k_sh = st.k[1]; p.k_sn = st.k[2];
@@ -100,28 +101,29 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
 
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
-           const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream,
-           const Split& sp = Split()) {
+           const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+           hipStream_t stream, const Split& sp = Split()) {
   if constexpr (sizeof(T) == 2 && (D == 96 || D == 128)) {
     static_assert(Shape16<D>::NW == 8, "the narrow shape halves an 8-wave workgroup");
     if (sp.n == 1 && causal && B * H * ((N + 255) / 256) < kNarrowBelowUnits)
-      return launch_shape<T, D, Shape16Narrow>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+      return launch_shape<T, D, Shape16Narrow>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream,
+                                                sp);
   }
-  return launch_shape<T, D, typename DefaultShape<T, D>::type>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len,
-                                                               stream, sp);
+  return launch_shape<T, D, typename DefaultShape<T, D>::type>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len,
+                                                               kv_len, stream, sp);
 }
 
 template <typename T>
 int dispatch_d(int64_t D, const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
-               int64_t N, const Strides& st, float scale, int causal, const int32_t* kv_len, hipStream_t stream,
-               const Split& sp = Split()) {
+               int64_t N, const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+               hipStream_t stream, const Split& sp = Split()) {
   switch (D) {
-    case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
-    case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
-    case 96: return launch<T, 96>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
-    case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+    case 32: return launch<T, 32>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream, sp);
+    case 64: return launch<T, 64>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream, sp);
+    case 96: return launch<T, 96>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream, sp);
+    case 128: return launch<T, 128>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream, sp);
     default:
-      if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, stream, sp);
+      if constexpr (sizeof(T) == 2) return launch<T, 256>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream, sp);
       return FA_ERR_UNSUPPORTED;
   }
 }
@@ -248,7 +250,7 @@ extern "C" const char* fa_strerror(int code) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid sizes (negative, or too large for the kernel's indexing)";
     case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (forward: f32, bf16, f16 with D 32, 64, 96, 128, and 256 for bf16/f16; backward: bf16, f16 with D 32, 64, 96, 128)";
-    case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE and kv_len 4 bytes)";
+    case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE, q_len and kv_len 4 bytes)";
     case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown error code";
@@ -260,8 +262,8 @@ namespace {
 // Checks shared by every forward entry point. Returns FA_OK and fills st, or an error;
 // *empty is set when there is nothing to compute (then nothing else is inspected).
 int validate_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
-                     int64_t N, int64_t D, const int64_t* strides, float scale, int causal, const int32_t* kv_len,
-                     int dtype, Strides& st, bool* empty) {
+                     int64_t N, int64_t D, const int64_t* strides, float scale, int causal, const int32_t* q_len,
+                     const int32_t* kv_len, int dtype, Strides& st, bool* empty) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
@@ -300,18 +302,18 @@ int validate_forward(const void* Q, const void* K, const void* V, void* O, float
   if (st.k[2] * elt > (int64_t(1) << 31) / kMaxBC || st.v[2] * elt > (int64_t(1) << 31) / kMaxBC) return FA_ERR_SHAPE;
   if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
   if (misaligned(Q, 16) || misaligned(K, 16) || misaligned(V, 16) || misaligned(O, 16)) return FA_ERR_ALIGN;
-  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4))) return FA_ERR_ALIGN;
+  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4)) || (q_len && misaligned(q_len, 4))) return FA_ERR_ALIGN;
   if (O == Q || O == K || O == V) return FA_ERR_ARG;
   return FA_OK;
 }
 
 int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
-                int64_t D, const Strides& st, float scale, int causal, const int32_t* kv_len, int dtype,
-                hipStream_t s, const Split& sp) {
+                int64_t D, const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+                int dtype, hipStream_t s, const Split& sp) {
   switch (dtype) {
-    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
-    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
-    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, kv_len, s, sp);
+    case FA_BF16: return dispatch_d<__bf16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, s, sp);
+    case FA_F16: return dispatch_d<_Float16>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, s, sp);
+    default: return dispatch_d<float>(D, Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, s, sp);
   }
 }
 
@@ -392,7 +394,7 @@ namespace {
 // the order Q, K, V, O, dO, dQ, dK, dV.
 int bwd_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
                void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, const int64_t st[8][3],
-               float scale, int causal, const int32_t* kv_len, int dtype, void* workspace,
+               float scale, int causal, const int32_t* q_len, const int32_t* kv_len, int dtype, void* workspace,
                int64_t workspace_bytes, void* stream, bool contiguous) {
   const int64_t need = fa_bwd_workspace_bytes(B, H, N, D);
   if (need < 0) return FA_ERR_SHAPE;
@@ -412,7 +414,9 @@ int bwd_common(const void* Q, const void* K, const void* V, const void* O, const
   if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV || !workspace) return FA_ERR_NULL;
   for (const void* ptr : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
     if (misaligned(ptr, 16)) return FA_ERR_ALIGN;
-  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4)) || misaligned(workspace, 256)) return FA_ERR_ALIGN;
+  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4)) || (q_len && misaligned(q_len, 4)) ||
+      misaligned(workspace, 256))
+    return FA_ERR_ALIGN;
   if (workspace_bytes < need) return FA_ERR_ARG;
   const int64_t tb = B * H * N * D * 2;
   if (contiguous) {
@@ -451,6 +455,7 @@ int bwd_common(const void* Q, const void* K, const void* V, const void* O, const
   fa::Strides3* ps[8] = {&p.st_q, &p.st_k, &p.st_v, &p.st_o, &p.st_do, &p.st_dq, &p.st_dk, &p.st_dv};
   for (int t = 0; t < 8; ++t) *ps[t] = fa::Strides3{st[t][0], st[t][1], st[t][2]};
   p.stats = static_cast<float*>(workspace);
+  p.q_len = q_len;
   p.kv_len = kv_len;
   p.H = H;
   p.N = N;
@@ -480,48 +485,42 @@ int bwd_precheck(int64_t B, int64_t H, int64_t N, int64_t D, float scale, int ca
 
 }  // namespace
 
-extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
-                      void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
-                      int causal, const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
-                      void* stream) {
+extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                              const void* dO, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
+                              int64_t D, const int64_t* strides, float scale, int causal, const int32_t* q_len,
+                              const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
   bool empty;
   const int rc = bwd_precheck(B, H, N, D, scale, causal, dtype, &empty);
   if (rc != FA_OK || empty) return rc;
   int64_t st[8][3];
   for (int t = 0; t < 8; ++t) {
-    st[t][0] = H * N * D;
-    st[t][1] = N * D;
-    st[t][2] = D;
+    for (int i = 0; i < 3; ++i) {
+      const int64_t contiguous_stride[3] = {H * N * D, N * D, D};
+      st[t][i] = strides ? strides[3 * t + i] : contiguous_stride[i];
+    }
   }
-  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, st, scale, causal, kv_len, dtype, workspace,
-                    workspace_bytes, stream, true);
+  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, st, scale, causal, q_len, kv_len, dtype, workspace,
+                    workspace_bytes, stream, strides == nullptr);
 }
 
-extern "C" int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-                              const void* dO, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
-                              int64_t D, const int64_t* strides, float scale, int causal, const int32_t* kv_len,
-                              int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!strides)
-    return fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype, workspace,
-                  workspace_bytes, stream);
-  bool empty;
-  const int rc = bwd_precheck(B, H, N, D, scale, causal, dtype, &empty);
-  if (rc != FA_OK || empty) return rc;
-  int64_t st[8][3];
-  for (int t = 0; t < 8; ++t)
-    for (int i = 0; i < 3; ++i) st[t][i] = strides[3 * t + i];
-  return bwd_common(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, st, scale, causal, kv_len, dtype, workspace,
-                    workspace_bytes, stream, false);
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* LSE, const void* dO,
+                      void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N, int64_t D, float scale,
+                      int causal, const int32_t* kv_len, int dtype, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+  return fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, nullptr, scale, causal, nullptr, kv_len, dtype,
+                        workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
                               int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
-                              const int32_t* kv_len, int dtype, void* stream) {
+                              const int32_t* q_len, const int32_t* kv_len, int dtype, void* stream) {
   Strides st;
   bool empty;
-  const int rc = validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, st, &empty);
+  const int rc =
+      validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, q_len, kv_len, dtype, st, &empty);
   if (rc != FA_OK || empty) return rc;
-  return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype,
+  return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, q_len, kv_len, dtype,
                      reinterpret_cast<hipStream_t>(stream), Split());
 }
 
@@ -535,15 +534,16 @@ extern "C" int64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N,
 
 extern "C" int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
                             int64_t H, int64_t N, int64_t D, const int64_t* strides, float scale, int causal,
-                            const int32_t* kv_len, int dtype, int n_splits, void* workspace,
+                            const int32_t* q_len, const int32_t* kv_len, int dtype, int n_splits, void* workspace,
                             int64_t workspace_bytes, void* stream) {
   if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_ARG;
   Strides st;
   bool empty;
-  int rc = validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, kv_len, dtype, st, &empty);
+  int rc = validate_forward(Q, K, V, O, LSE, B, H, N, D, strides, scale, causal, q_len, kv_len, dtype, st, &empty);
   if (rc != FA_OK || empty) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (n_splits == 1) return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype, s, Split());
+  if (n_splits == 1)
+    return run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, q_len, kv_len, dtype, s, Split());
   const int64_t need = fa_fwd_split_workspace_bytes(B, H, N, D, n_splits);
   if (need < 0) return FA_ERR_SHAPE;
   if (!workspace) return FA_ERR_NULL;
@@ -553,7 +553,7 @@ extern "C" int fa_fwd_split(const void* Q, const void* K, const void* V, void* O
   sp.n = n_splits;
   sp.part_o = static_cast<float*>(workspace);
   sp.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_o_bytes(n_splits, B * H * N, D));
-  rc = run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, kv_len, dtype, s, sp);
+  rc = run_forward(Q, K, V, O, LSE, B, H, N, D, st, scale, causal, q_len, kv_len, dtype, s, sp);
   if (rc != FA_OK) return rc;
   return run_merge(sp.part_o, sp.part_lse, n_splits, B, H, N, D, O, st.o, LSE, dtype, s);
 }
@@ -608,5 +608,5 @@ extern "C" int fa_merge_states(const float* part_o, const float* part_lse, int n
 extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
                       int64_t N, int64_t D, float scale, int causal, const int32_t* kv_len, int dtype,
                       void* stream) {
-  return fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, nullptr, scale, causal, kv_len, dtype, stream);
+  return fa_fwd_strided(Q, K, V, O, LSE, B, H, N, D, nullptr, scale, causal, nullptr, kv_len, dtype, stream);
 }

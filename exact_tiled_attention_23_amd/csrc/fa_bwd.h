@@ -62,7 +62,8 @@ struct BwdParams {
   void* dv;
   Strides3 st_q, st_k, st_v, st_o, st_do, st_dq, st_dk, st_dv;
   float* stats;       // [B*H][ceil(N/64)][128] floats: 64 exponent offsets, then 64 Delta values
-  const int32_t* kv_len;
+  const int32_t* kv_len;  // nullable: keys at or past kv_len[b] are padding
+  const int32_t* q_len;   // nullable: query rows at or past q_len[b] are padding (not read, dQ = 0)
   int64_t H, N;
   float scale;
   float scale_log2;   // scale * log2(e)
@@ -203,19 +204,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int x = p.kv_len[b];
     kvl = x < 0 ? 0 : (x > n ? n : x);
   }
+  int nq = n;  // rows at or past nq are query padding
+  if (p.q_len) {
+    const int x = p.q_len[b];
+    nq = x < 0 ? 0 : (x > n ? n : x);
+  }
   int kv_hi = kvl, wave_hi = kvl;
   if (p.causal) {
-    kv_hi = min(kv_hi, q0 + BR);
-    wave_hi = min(wave_hi, qw + 32);
+    kv_hi = min(min(kv_hi, q0 + BR), nq);
+    wave_hi = min(min(wave_hi, qw + 32), nq);
   }
+  if (q0 >= nq) kv_hi = 0;
+  if (qw >= nq) wave_hi = 0;
+  kv_hi = __builtin_amdgcn_readfirstlane(kv_hi);    // wave-uniform: keep the tile tests scalar
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
   const int ntiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
 
-  // ---- Q^T and dO^T fragments (B operands), Delta = rowsum(dO o O), exponent offset.
+  // ---- Q^T and dO^T fragments (B operands), Delta = rowsum(dO o O), exponent offset. A
+  // padding row is not read: zero fragments, Delta 0 and an empty row's offset make its P, dS
+  // and dQ exactly 0.
   frag qf[NQF], dof[NQF];
   float dsum = 0.f;
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
-    if (qrow < n) {
+    if (qrow < nq) {
       qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * p.st_q.n + 16 * s + 8 * g);
       dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * p.st_do.n + 16 * s + 8 * g);
       const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * p.st_o.n + 16 * s + 8 * g);
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   const float delta = pair_sum(dsum);
-  const float lse = qrow < n ? p.lse[(int64_t)bh * n + qrow] : -INFINITY;
+  const float lse = qrow < nq ? p.lse[(int64_t)bh * n + qrow] : -INFINITY;
   // P = 2^(s*c - mo): +inf offset for a row with no valid key (its P is 0).
   const float mo = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
   {
@@ -406,8 +418,14 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int x = p.kv_len[b];
     kvl = x < 0 ? 0 : (x > n ? n : x);
   }
-  // Query tiles that can see some key of this tile: all of them, or from the diagonal on.
-  const int nqt = k0 < kvl ? (n + BQ - 1) / BQ : 0;
+  int nq = n;  // rows at or past nq are query padding
+  if (p.q_len) {
+    const int x = p.q_len[b];
+    nq = x < 0 ? 0 : (x > n ? n : x);
+  }
+  // Query tiles that can see some key of this tile: all of them up to the last present row,
+  // or from the diagonal on.
+  const int nqt = k0 < kvl ? (nq + BQ - 1) / BQ : 0;
   const int t0 = p.causal ? k0 / BQ : 0;
 
   // ---- K^T and V^T fragments (B operands) of this lane's key; zero past kv_len, where
@@ -453,6 +471,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     const unsigned char* ob = qb + TILEB;
     const float* sb = reinterpret_cast<const float*>(qb + 2 * TILEB);
     wait_vmem();
+    if (i0 + BQ > nq) {
+      // Padding query rows may hold anything: zero them so 0 * garbage cannot reach dK, dV.
+      plan.zero_from(lds + buf * BUFB, nq - i0, wave, lane);
+      plan.zero_from(lds + buf * BUFB + TILEB, nq - i0, wave, lane);
+    }
     __syncthreads();
     if (t + 1 < nqt) issue(t + 1, buf ^ 1);
 
@@ -623,7 +646,12 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
     const int x = p.kv_len[b];
     kvl = x < 0 ? 0 : (x > n ? n : x);
   }
-  const int nqt = k0 < kvl ? (n + BQ - 1) / BQ : 0;
+  int nq = n;  // rows at or past nq are query padding
+  if (p.q_len) {
+    const int x = p.q_len[b];
+    nq = x < 0 ? 0 : (x > n ? n : x);
+  }
+  const int nqt = k0 < kvl ? (nq + BQ - 1) / BQ : 0;
   const int t0 = p.causal ? k0 / BQ : 0;
   const bool key_dead = key >= kvl;
 
@@ -667,6 +695,11 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
     const unsigned char* ob = qb + QTB;
     const float* sb = reinterpret_cast<const float*>(qb + 2 * QTB);
     if (t > t0) wait_vmem();
+    if (i0 + BQ > nq) {
+      // Padding query rows may hold anything: zero them so 0 * garbage cannot reach dK, dV.
+      qplan.zero_from(qbuf + buf * BUFB, nq - i0, wave, lane);
+      qplan.zero_from(qbuf + buf * BUFB + QTB, nq - i0, wave, lane);
+    }
     __syncthreads();
     if (t + 1 < nqt) issue(t + 1, buf ^ 1);
 

@@ -69,7 +69,8 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;             // contiguous [B][H][N]
-  const int32_t* kv_len;  // nullable
+  const int32_t* kv_len;  // nullable: keys at or past kv_len[b] are padding
+  const int32_t* q_len;   // nullable: query rows at or past q_len[b] are padding (O = 0, LSE = -inf)
   // Element strides of the batch, head and token dimensions (the head dimension D is
   // contiguous): tensor X element (b, h, n, d) lives at X + b*x_sb + h*x_sh + n*x_sn + d.
   int64_t q_sb, q_sh, q_sn;
@@ -182,13 +183,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     int64_t x = p.kv_len[b];
     kvl = x < 0 ? 0 : (x > N ? N : x);
   }
+  int64_t nq = N;  // rows at or past nq are query padding: no key, O = 0, LSE = -inf
+  if (p.q_len) {
+    int64_t x = p.q_len[b];
+    nq = x < 0 ? 0 : (x > N ? N : x);
+  }
   // Keys any row of this tile may see, and keys any row of this wave may see.
   int64_t kv_hi = kvl;
   int64_t wave_hi = kvl;
   if (p.causal) {
     kv_hi = kv_hi < q0 + BR ? kv_hi : q0 + BR;
     wave_hi = wave_hi < qw + 32 ? wave_hi : qw + 32;
+    kv_hi = kv_hi < nq ? kv_hi : nq;
+    wave_hi = wave_hi < nq ? wave_hi : nq;
   }
+  if (q0 >= nq) kv_hi = 0;
+  if (qw >= nq) wave_hi = 0;
   // Key tiles [t_lo, t_hi) of this unit's split.
   const int all_tiles = kv_hi > 0 ? (int)((kv_hi + BC - 1) / BC) : 0;
   const int chunk = (all_tiles + p.n_splits - 1) / p.n_splits;
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   frag qf[NQF];
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
-    if (qrow < N) {
+    if (qrow < nq) {  // padding rows are not read (they may hold anything)
       qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + KSTEP * s + KPER * g);
     } else {
       qf[s] = frag{};
@@ -301,14 +311,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       }
 
       // ---- masks: only where the tile crosses the kv_len edge or this wave's diagonal
-      const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw);
+      const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq;
       if (need_mask) {
 #pragma unroll
         for (int u = 0; u < NSUB; ++u) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int64_t key = j0 + 32 * u + acc_key<KPER>(i, g);
-            const bool dead = key >= kvl || (p.causal && key > qrow);
+            const bool dead = key >= kvl || (p.causal && key > qrow) || qrow >= nq;
             if (dead) s[u][i] = -INFINITY;
           }
         }

@@ -29,6 +29,9 @@
 //    addressed 2); fully masked rows end with l = 0 and store O = 0, LSE = -inf.
 //  * Padding keys (>= kv_len) in the edge tile: their V rows are zeroed in LDS after
 //    the load so garbage past kv_len cannot reach O, and their scores are masked.
+//  * Padding queries (>= q_len): their Q rows are not read and every score of theirs is
+//    masked, so they end as fully masked rows; tiles and waves made only of padding rows
+//    skip the key loop.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -158,11 +161,22 @@ void fwd16_kernel(FwdParams p) {
     const int x = p.kv_len[b];
     kvl = x < 0 ? 0 : (x > n ? n : x);
   }
+  int nq = n;  // rows at or past nq are query padding: no key, O = 0, LSE = -inf
+  if (p.q_len) {
+    const int x = p.q_len[b];
+    nq = x < 0 ? 0 : (x > n ? n : x);
+  }
   int kv_hi = kvl, wave_hi = kvl;
   if (p.causal) {
-    kv_hi = min(kv_hi, q0 + BR);
-    wave_hi = min(wave_hi, qw + 32);
+    kv_hi = min(min(kv_hi, q0 + BR), nq);
+    wave_hi = min(min(wave_hi, qw + 32), nq);
   }
+  if (q0 >= nq) kv_hi = 0;
+  if (qw >= nq) wave_hi = 0;
+  // Both bounds are wave-uniform; saying so keeps the per-tile tests on them scalar branches
+  // (the compiler otherwise forms the three-way minimum in a vector register).
+  kv_hi = __builtin_amdgcn_readfirstlane(kv_hi);
+  wave_hi = __builtin_amdgcn_readfirstlane(wave_hi);
   // Key tiles [t_lo, t_hi) of this unit's split (all of them without a split).
   const int all_tiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
   const int ns = SPLIT ? p.n_splits : 1;
@@ -220,8 +234,8 @@ void fwd16_kernel(FwdParams p) {
   frag qf[NQF];
 #pragma unroll
   for (int s = 0; s < NQF; ++s) {
-    if (qrow < n) qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + 16 * s + 8 * g);
-    else qf[s] = frag{};
+    if (qrow < nq) qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + 16 * s + 8 * g);
+    else qf[s] = frag{};  // padding rows are not read (they may hold anything)
   }
   // Consume the Q fragments here, so the compiler's wait for them is placed before the
   // loop rather than re-issued (as a full vmcnt wait) in every iteration.
@@ -306,10 +320,11 @@ void fwd16_kernel(FwdParams p) {
         }
       }
 
-      // ---- masks (edge tiles only): key j0 + 32u + acc_key(i, g) is dead when it is at
-      // or past kv_len, or (causal) after this lane's query.
-      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw)) {
-        int lim = kvl - j0;
+      // ---- masks (edge tiles, and every tile of the wave that holds the last query rows
+      // before padding): key j0 + 32u + acc_key(i, g) is dead when it is at or past kv_len,
+      // or (causal) after this lane's query, or this lane's query is padding.
+      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq) {
+        int lim = qrow < nq ? kvl - j0 : 0;
         if (p.causal) lim = min(lim, qrow - j0 + 1);
         lim -= 8 * g;
 #pragma unroll

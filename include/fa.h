@@ -89,12 +89,19 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
  *           query heads); O must not (no two (b, h, n, d) may name the same element).
  *           K and V token strides may not exceed 16 MiB. LSE stays contiguous [B][H][N].
  * D       : 32, 64, 96 or 128 for every dtype; 256 for FA_BF16 and FA_F16.
+ * q_len   : device pointer to int32[B], the number of query rows present in each batch
+ *           element, or NULL for N everywhere (values outside [0, N] are clamped by the
+ *           kernel). Query-side padding, the pages' hardened masking for padding applied to
+ *           queries: a row at or past q_len[b] attends to nothing, its Q row is not read
+ *           (it may hold anything), and it is written as O = 0, LSE = -inf. The causal mask is
+ *           unchanged (row i sees keys j <= i). 4-byte aligned.
  * Other arguments, ownership and errors as fa_fwd; a negative stride or an overlapping O
  * gives FA_ERR_ARG, a misaligned stride FA_ERR_ALIGN.
  */
 int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE,
                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
-                   float scale, int causal, const int32_t* kv_len, int dtype, void* stream);
+                   float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+                   int dtype, void* stream);
 
 /*
  * fa_fwd_split_workspace_bytes - device workspace that fa_fwd_split needs for these sizes
@@ -129,8 +136,9 @@ int64_t fa_fwd_split_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D,
  */
 int fa_fwd_split(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
-                 float scale, int causal, const int32_t* kv_len, int dtype, int n_splits,
-                 void* workspace, int64_t workspace_bytes, void* stream);
+                 float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+                 int dtype, int n_splits, void* workspace, int64_t workspace_bytes,
+                 void* stream);
 
 /*
  * fa_fwd_split_count - a suggested n_splits for fa_fwd_split on the current HIP device.
@@ -225,13 +233,17 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
  *           per query head, which the caller sums over the heads that share one). dQ, dK and dV
  *           must not overlap themselves (FA_ERR_ARG), nor each other or any input; only an
  *           output starting at an input, another output or the workspace is detected.
+ * q_len   : device pointer to int32[B] or NULL, as for fa_fwd_strided (pass the forward's
+ *           q_len). Rows at or past q_len[b] are not part of the batch element: their rows of
+ *           Q, O and dO are not read (they may hold anything, NaN included), their dQ rows are
+ *           written as 0, and they add nothing to dK or dV. 4-byte aligned.
  * LSE and the workspace stay contiguous. Other arguments and errors as fa_bwd.
  */
 int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
                    const void* dO, void* dQ, void* dK, void* dV,
                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
-                   float scale, int causal, const int32_t* kv_len, int dtype, void* workspace,
-                   int64_t workspace_bytes, void* stream);
+                   float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
+                   int dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);

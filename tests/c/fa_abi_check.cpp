@@ -56,7 +56,7 @@ float pattern(int i, int salt) { return (float)(((i * 37 + salt * 101) % 33) - 1
 
 int main() {
   std::printf("fa ABI version %d\n", fa_abi_version());
-  check(fa_abi_version() >= 4, "ABI version");
+  check(fa_abi_version() >= 6, "ABI version");
   check(fa_fwd(nullptr, nullptr, nullptr, nullptr, nullptr, 1, 1, 8, 64, 0.125f, 1, nullptr, FA_BF16, nullptr) ==
             FA_ERR_NULL, "NULL pointers rejected");
   check(std::strlen(fa_strerror(FA_ERR_ALIGN)) > 0, "strerror text");
@@ -128,9 +128,9 @@ int main() {
   const int S = 3;
   const int64_t wsb = fa_fwd_split_workspace_bytes(B, H, N, D, S);
   HIP_OK(hipMalloc(&ws, wsb));
-  check(fa_fwd_split(q, k, v, o2, lse2, B, H, N, D, nullptr, scale, 0, nullptr, FA_BF16, S, ws, wsb, nullptr) ==
+  check(fa_fwd_split(q, k, v, o2, lse2, B, H, N, D, nullptr, scale, 0, nullptr, nullptr, FA_BF16, S, ws, wsb, nullptr) ==
             FA_OK, "fa_fwd_split");
-  check(fa_fwd_split(q, k, v, o2, lse2, B, H, N, D, nullptr, scale, 0, nullptr, FA_BF16, S, ws, wsb - 1, nullptr) ==
+  check(fa_fwd_split(q, k, v, o2, lse2, B, H, N, D, nullptr, scale, 0, nullptr, nullptr, FA_BF16, S, ws, wsb - 1, nullptr) ==
             FA_ERR_ARG, "fa_fwd_split rejects a short workspace");
   HIP_OK(hipDeviceSynchronize());
   std::vector<uint16_t> ho2(elems);

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 5
+    assert fa.fa_abi_version() == 6
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -136,7 +136,17 @@ def call_strided(strides, dtype=None, **kw):
     a = dict(GOOD, B=B_, H=H_, N=N_, D=D_)
     a.update(kw)
     return fa.fa_fwd_strided(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["D"], strides,
-                             a["scale"], a["causal"], a["kv_len"], a["dtype"] if dtype is None else dtype, a["stream"])
+                             a["scale"], a["causal"], a.get("q_len", 0), a["kv_len"],
+                             a["dtype"] if dtype is None else dtype, a["stream"])
+
+
+def test_q_len_alignment_and_null():
+    """q_len is a nullable 4-byte-aligned device pointer on every entry point that takes it."""
+    assert call_strided(None, q_len=A + 0x600 + 2) == binding.FA_ERR_ALIGN
+    assert call_split(q_len=A + 0x600 + 1) == binding.FA_ERR_ALIGN
+    assert call_bwd_strided(None, q_len=A + 0x600 + 2) == binding.FA_ERR_ALIGN
+    # empty problems return before any pointer is inspected
+    assert call_strided(None, q_len=A + 0x600 + 2, N=0) == binding.FA_OK
 
 
 @pytest.mark.parametrize("i", range(12))
@@ -221,8 +231,8 @@ def call_split(n_splits=2, workspace=WS, workspace_bytes=None, **kw):
     if workspace_bytes is None:
         workspace_bytes = max(0, ws_formula(a["B"], a["H"], a["N"], a["D"], n_splits))
     return fa.fa_fwd_split(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["N"], a["D"], None,
-                           a["scale"], a["causal"], a["kv_len"], a["dtype"], n_splits, workspace, workspace_bytes,
-                           a["stream"])
+                           a["scale"], a["causal"], a.get("q_len", 0), a["kv_len"], a["dtype"], n_splits, workspace,
+                           workspace_bytes, a["stream"])
 
 
 @pytest.mark.parametrize("S", [0, -3, 257])
@@ -353,8 +363,8 @@ def call_bwd_strided(strides, **kw):
     a = dict(BG)
     a.update(kw)
     return fa.fa_bwd_strided(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dO"], a["dQ"], a["dK"], a["dV"], a["B"],
-                             a["H"], a["N"], a["D"], strides, a["scale"], a["causal"], a["kv_len"], a["dtype"],
-                             a["ws"], a["ws_bytes"], a["stream"])
+                             a["H"], a["N"], a["D"], strides, a["scale"], a["causal"], a.get("q_len", 0), a["kv_len"],
+                             a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("i", range(24))

@@ -1,0 +1,152 @@
+"""GPU parity of query-side padding (q_len) against the oracle, forward and backward.
+
+A query row at or past q_len[b] is not part of the batch element: the forward writes O = 0,
+LSE = -inf for it, and the backward gives it dQ = 0 and takes nothing from it into dK, dV.
+Its rows of Q (and, for the backward, of O and dO) are filled with NaN here, so any read of
+them would show. Tolerances are those of the forward and backward parity tests; the gradient
+bound is evaluated on inputs whose padding rows are zero, which by the definition give the same
+gradients.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_23_amd as fa
+from exact_tiled_attention_23_amd.workloads import generate, generate_grad_output, to_f64
+
+from test_backward_gpu import DTYPE_NAME, compare_grad, rounding_bound
+from test_parity_gpu import compare, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _pad_rows(t, q_len, value):
+    t = t.clone()
+    for b, L in enumerate(q_len):
+        t[b, :, int(L):] = value
+    return t
+
+
+def _forward_case(B, H, N, D, dtype, causal, q_len, kv_len, seed, n_splits=1):
+    x = generate(B, H, N, D, dtype, causal=causal, seed=seed)
+    q_nan = _pad_rows(x.q, q_len, float("nan"))
+    q, k, v = (t.to(DEV) for t in (q_nan, x.k, x.v))
+    ql = torch.as_tensor(q_len, dtype=torch.int32)
+    kl = None if kv_len is None else torch.as_tensor(kv_len, dtype=torch.int32)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=x.scale, kv_len=kl, q_len=ql, out=o, lse=lse,
+                        n_splits=n_splits)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal, kv_len=kv_len,
+                              q_len=q_len)
+    tag = f"B={B} N={N} D={D} {dtype} causal={causal} q_len={list(q_len)} kv={kv_len} S={n_splits}"
+    compare(o, lse, ro, rl, dtype, tag)
+    for b, L in enumerate(q_len):
+        assert (o[b, :, int(L):] == 0).all().item(), "padding rows of O must be exactly 0 " + tag
+        pl = lse[b, :, int(L):]
+        assert (torch.isinf(pl) & (pl < 0)).all().item(), "padding rows of LSE must be -inf " + tag
+    return x, o, lse
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 96), ("bf16", 64), ("bf16", 96), ("bf16", 128),
+                                     ("f16", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_query_padding(dtype, D, causal):
+    """q_len 0, 1, a tile edge, ragged and N, with and without key padding."""
+    q_len = np.array([0, 1, 128, 201, 300], dtype=np.int32)
+    for kv in (None, np.array([300, 150, 64, 1, 300], dtype=np.int32)):
+        say(f"query padding forward {dtype} D={D} causal={causal} kv={kv}")
+        _forward_case(5, 2, 300, D, dtype, causal, q_len, kv, seed=4300 + D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_query_padding_split(causal):
+    q_len = np.array([700, 333, 0], dtype=np.int32)
+    for S in (2, 5):
+        say(f"query padding split S={S} causal={causal}")
+        _forward_case(3, 2, 700, 128, "bf16", causal, q_len, None, seed=4400, n_splits=S)
+
+
+def test_forward_query_padding_large_sampled():
+    """B=2 H=8 N=4096 D=128 bf16 causal, q_len 4096 and 1000: sampled rows on both sides of the
+    boundary against the oracle, exact zeros past it."""
+    B, H, N, D = 2, 8, 4096, 128
+    q_len = np.array([4096, 1000], dtype=np.int32)
+    x = generate(B, H, N, D, "bf16", causal=True, seed=4500)
+    q = _pad_rows(x.q, q_len, float("nan")).to(DEV)
+    o, lse = fa.forward(q, x.k.to(DEV), x.v.to(DEV), causal=True, scale=x.scale,
+                        q_len=torch.as_tensor(q_len, dtype=torch.int32))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 999, 1000, 1001, 2047, 4095])
+    for b, h in [(0, 3), (1, 0), (1, 7)]:
+        say(f"query padding large b={b} h={h}")
+        ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
+                                  to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=True, rows=rows,
+                                  q_len=q_len[b:b + 1])
+        compare(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], ro, rl, "bf16", f"b={b} h={h}")
+    assert (o[1, :, 1000:] == 0).all().item() and torch.isinf(lse[1, :, 1000:]).all().item()
+
+
+def _backward_case(B, H, N, D, dtype, causal, q_len, kv_len, seed):
+    x = generate(B, H, N, D, dtype, causal=causal, seed=seed)
+    do = generate_grad_output(B, H, N, D, dtype, seed=seed + 1)
+    ql = torch.as_tensor(q_len, dtype=torch.int32)
+    kl = None if kv_len is None else torch.as_tensor(kv_len, dtype=torch.int32)
+    q = _pad_rows(x.q, q_len, float("nan")).to(DEV)
+    k, v = x.k.to(DEV), x.v.to(DEV)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=x.scale, kv_len=kl, q_len=ql)
+    o = _pad_rows(o, q_len, float("nan"))                 # padding rows of O are not read either
+    dO = _pad_rows(do, q_len, float("nan")).to(DEV)
+    grads = [torch.full_like(q, float("nan")) for _ in range(3)]
+    dq, dk, dv = fa.backward(q, k, v, o, lse, dO, causal=causal, scale=x.scale, kv_len=kl, q_len=ql,
+                             dq=grads[0], dk=grads[1], dv=grads[2])
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = to_f64(x.q), to_f64(x.k), to_f64(x.v), to_f64(do)
+    ref = oracle.attention_grad(q64, k64, v64, do64, x.scale, causal=causal, kv_len=kv_len, q_len=q_len)
+    zq = q64.copy()
+    zdo = do64.copy()
+    for b, L in enumerate(q_len):
+        zq[b, :, int(L):] = 0.0
+        zdo[b, :, int(L):] = 0.0
+    T = rounding_bound(zq, k64, v64, zdo, x.scale, causal, kv_len, dtype)
+    tag = f"B={B} N={N} D={D} {dtype} causal={causal} q_len={list(q_len)} kv={kv_len}"
+    for g, r, t, name in zip((dq, dk, dv), ref, T, ("dQ", "dK", "dV")):
+        compare_grad(g, r, t, dtype, f"{tag} {name}")
+    for b, L in enumerate(q_len):
+        assert (dq[b, :, int(L):] == 0).all().item(), "padding rows of dQ must be exactly 0 " + tag
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 96), ("bf16", 128), ("f16", 64), ("f16", 128),
+                                     ("bf16", 32)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_query_padding(dtype, D, causal):
+    """q_len 0, 1, a tile edge, ragged and N, NaN in the padding rows of Q, O and dO."""
+    q_len = np.array([0, 1, 128, 201], dtype=np.int32)
+    for kv in (None, np.array([201, 100, 64, 150], dtype=np.int32)):
+        say(f"query padding backward {dtype} D={D} causal={causal} kv={kv}")
+        _backward_case(4, 2, 201, D, dtype, causal, q_len, kv, seed=4600 + D)
+
+
+def test_autograd_with_query_padding():
+    B, H, N, D = 2, 2, 150, 64
+    x = generate(B, H, N, D, "bf16", causal=True, seed=4700)
+    q_len = np.array([150, 77], dtype=np.int32)
+    q = x.q.to(DEV).requires_grad_(True)
+    k = x.k.to(DEV).requires_grad_(True)
+    v = x.v.to(DEV).requires_grad_(True)
+    o = fa.attention(q, k, v, causal=True, scale=x.scale, q_len=q_len)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=4701)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    dq, dk, dv = fa.backward(q.detach(), k.detach(), v.detach(), *fa.forward(q.detach(), k.detach(), v.detach(),
+                                                                             causal=True, scale=x.scale,
+                                                                             q_len=q_len),
+                             do.to(DEV), causal=True, scale=x.scale, q_len=q_len)
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad, dq) and torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+    assert (q.grad[1, :, 77:] == 0).all().item()
