@@ -88,7 +88,6 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
   if (n_qtiles > INT32_MAX || units > INT32_MAX) return FA_ERR_SHAPE;
   p.n_qtiles = (int)n_qtiles;
   p.n_units = units;
-  p.xcd_groups = (units % 8 == 0) ? 8 : 1;
   p.n_splits = sp.n;
   p.BH = B * H;
   p.part_o = sp.part_o;
@@ -352,7 +351,6 @@ int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipSt
   fa::BwdParams p = base;
   p.n_tiles = (int)tiles;
   p.n_units = units;
-  p.xcd_groups = (units % 8 == 0) ? 8 : 1;
   void* args[] = {&p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>),
                                  dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);

@@ -70,7 +70,6 @@ struct BwdParams {
   int causal;
   int n_tiles;        // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
   int64_t n_units;    // B * H * n_tiles
-  int xcd_groups;     // 8 when n_units % 8 == 0, else 1
 };
 
 constexpr int kStatRows = 64;  // rows per block of the stats array
@@ -85,8 +84,7 @@ template <int D> __device__ __forceinline__ int swz_u(int j) {
 }
 
 __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh) {
-  int unit = bid;
-  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
+  const int unit = xcd_unit(bid, p.n_units);  // a head's tiles on one XCD (fa_fwd_kernel.h)
   *bh = unit / p.n_tiles;
   return unit % p.n_tiles;
 }

@@ -83,7 +83,6 @@ struct FwdParams {
   int causal;
   int n_qtiles;           // ceil(N / BR)
   int64_t n_units;        // B * H * n_qtiles * n_splits (the grid size)
-  int xcd_groups;         // 8 when n_units % 8 == 0, else 1
   // Key-axis split: with n_splits > 1 the work unit also names a split s. A query tile
   // with T visible key tiles gives split s the tiles [s*c, min(T, (s+1)*c)), c = ceil(T/S),
   // and the epilogue stores that split's normalised partial state (O_s in float32, LSE_s)
@@ -94,17 +93,25 @@ struct FwdParams {
   float* part_lse;
 };
 
-// Work unit -> (bh, query tile, split). Heads are grouped per XCD (blocks are dispatched
-// round-robin over the 8 XCDs) so the query tiles of a head share one L2; causal runs the
-// longest query tiles first.
+// Work unit of workgroup `bid`. The dispatcher hands workgroups to the 8 XCDs in turn (bid mod
+// 8), and each XCD has its own L2. Numbering each XCD's workgroups as one contiguous run of units
+// keeps consecutive units (the query tiles of one head) on one XCD, so a head's K/V tiles come
+// from HBM once. With n_units = 8q + r, XCD x takes units [xq + min(x, r), ... + q + (x < r)):
+// a bijection of [0, n_units) for any unit count (only locality depends on the dispatch order).
+__device__ __forceinline__ int xcd_unit(int bid, int64_t n_units) {
+  const int q = (int)(n_units / 8), r = (int)(n_units % 8);
+  const int x = bid % 8;
+  return x * q + min(x, r) + bid / 8;
+}
+
+// Work unit -> (bh, query tile, split); causal runs the longest query tiles first.
 struct Unit {
   int bh, qt, split;
 };
 // SPLIT = false compiles the unsplit case (n_splits == 1) without the split arithmetic.
 template <bool SPLIT>
 __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
-  int unit = bid;
-  if (p.xcd_groups == 8) unit = (unit % 8) * (int)(p.n_units / 8) + unit / 8;
+  const int unit = xcd_unit(bid, p.n_units);
   Unit u;
   const int ns = SPLIT ? p.n_splits : 1;
   const int per_head = p.n_qtiles * ns;
