@@ -85,7 +85,8 @@ template <int D> __device__ __forceinline__ int swz_u(int j) {
 
 __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh) {
   const int unit = xcd_unit(bid, p.n_units);  // a head's tiles on one XCD (fa_fwd_kernel.h)
-  *bh = unit / p.n_tiles;
+  const int heads = (int)(p.n_units / p.n_tiles);
+  *bh = head_of_slot(unit / p.n_tiles, heads / (int)p.H, (int)p.H);
   return unit % p.n_tiles;
 }
 

@@ -104,6 +104,14 @@ __device__ __forceinline__ int xcd_unit(int bid, int64_t n_units) {
   return x * q + min(x, r) + bid / 8;
 }
 
+// (b, h) of head slot `slot` (slots are the consecutive runs of units that one head's tiles
+// occupy). Slots run over the batch fastest, so the run of slots an XCD takes holds heads of
+// every batch element: with per-batch key padding the work of an element varies, and a slot
+// order by batch would give whole elements, and so unequal work, to single XCDs.
+__device__ __forceinline__ int head_of_slot(int slot, int B, int H) {
+  return (slot % B) * H + slot / B;
+}
+
 // Work unit -> (bh, query tile, split); causal runs the longest query tiles first.
 struct Unit {
   int bh, qt, split;
@@ -115,7 +123,7 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   Unit u;
   const int ns = SPLIT ? p.n_splits : 1;
   const int per_head = p.n_qtiles * ns;
-  u.bh = unit / per_head;
+  u.bh = head_of_slot(unit / per_head, (int)(p.BH / p.H), (int)p.H);
   const int rem = unit % per_head;
   u.qt = rem / ns;
   u.split = rem % ns;
