@@ -84,10 +84,12 @@ template <int D> __device__ __forceinline__ int swz_u(int j) {
 }
 
 __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh) {
-  const int unit = xcd_unit(bid, p.n_units);  // a head's tiles on one XCD (fa_fwd_kernel.h)
+  // a head's tiles on one XCD, longest first (fa_fwd_kernel.h)
   const int heads = (int)(p.n_units / p.n_tiles);
-  *bh = head_of_slot(unit / p.n_tiles, heads / (int)p.H, (int)p.H);
-  return unit % p.n_tiles;
+  int slot, rank;
+  unit_slot(bid, p.n_units, heads, p.n_tiles, p.causal && !p.kv_len && !p.q_len, &slot, &rank);
+  *bh = head_of_slot(slot, heads / (int)p.H, (int)p.H);
+  return rank;
 }
 
 // Per-lane copy plan of a [rows][D] tile into LDS, 1 KB per copy instruction: copy i of this

@@ -117,14 +117,38 @@ struct Unit {
   int bh, qt, split;
 };
 // SPLIT = false compiles the unsplit case (n_splits == 1) without the split arithmetic.
+// Head slot and rank within the head (0 first) of workgroup `bid`, for `heads` heads of
+// `per_head` units each. Each XCD takes a contiguous run of heads (xcd_unit). Within an XCD the
+// units go head by head, or, with `tile_major` and whole heads on every XCD (heads % 8 == 0),
+// rank by rank over the XCD's heads. Under the causal mask a head's units shrink from the first
+// rank to the last. Head by head, the next head's long units start behind the previous head's
+// short ones, and with few units per head the XCD's last long unit ends late; rank by rank is
+// the longest-first order. It is used only when every head has the same work (no per-batch
+// padding, since with padding the ranks of different heads are not comparable) and heads are
+// short (at most kTileMajorUnits units: with longer heads head by head is already balanced and
+// keeps fewer heads' K/V in the XCD's L2 at a time).
+constexpr int kTileMajorUnits = 32;
+__device__ __forceinline__ void unit_slot(int bid, int64_t n_units, int heads, int per_head, bool tile_major,
+                                          int* slot, int* rank) {
+  if (tile_major && heads % 8 == 0 && per_head <= kTileMajorUnits) {
+    const int hx = heads / 8, i = bid / 8;
+    *slot = (bid % 8) * hx + i % hx;
+    *rank = i / hx;
+  } else {
+    const int unit = xcd_unit(bid, n_units);
+    *slot = unit / per_head;
+    *rank = unit % per_head;
+  }
+}
+
 template <bool SPLIT>
 __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
-  const int unit = xcd_unit(bid, p.n_units);
   Unit u;
   const int ns = SPLIT ? p.n_splits : 1;
   const int per_head = p.n_qtiles * ns;
-  u.bh = head_of_slot(unit / per_head, (int)(p.BH / p.H), (int)p.H);
-  const int rem = unit % per_head;
+  int slot, rem;
+  unit_slot(bid, p.n_units, (int)p.BH, per_head, p.causal && !p.kv_len && !p.q_len, &slot, &rem);
+  u.bh = head_of_slot(slot, (int)(p.BH / p.H), (int)p.H);
   u.qt = rem / ns;
   u.split = rem % ns;
   if (p.causal) u.qt = p.n_qtiles - 1 - u.qt;
