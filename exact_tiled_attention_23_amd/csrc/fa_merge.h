@@ -43,16 +43,19 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
   if (m != -INFINITY) {
+    // Every state's loads are issued without a branch (so they overlap); an identity state
+    // (LSE = -inf) is dropped by selection, not by a zero weight, since its O may be anything.
+#pragma unroll 4
     for (int s = 0; s < p.n_states; ++s) {
       const float ls = p.part_lse[s * p.rows + row];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - m);
       const float4 x = *reinterpret_cast<const float4*>(p.part_o + (s * p.rows + row) * D + c);
+      const bool live = ls != -INFINITY;
+      const float w = live ? expf(ls - m) : 0.f;
       sum += w;
-      acc.x += w * x.x;
-      acc.y += w * x.y;
-      acc.z += w * x.z;
-      acc.w += w * x.w;
+      acc.x = live ? acc.x + w * x.x : acc.x;
+      acc.y = live ? acc.y + w * x.y : acc.y;
+      acc.z = live ? acc.z + w * x.z : acc.z;
+      acc.w = live ? acc.w + w * x.w : acc.w;
     }
   }
   const float inv = (sum == 0.f) ? 0.f : 1.f / sum;
