@@ -23,6 +23,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-parameter",
     # Packed fp32 VALU instructions are kept out of every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Loop headers start on a 64-byte boundary, so a kernel's main loop keeps its alignment when
+    # code before it changes (an unaligned forward loop measured about 1.5% slower).
+    "-falign-loops=64",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -88,7 +88,8 @@ __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh)
   const int heads = (int)(p.n_units / p.n_tiles);
   int slot, rank;
   unit_slot(bid, p.n_units, heads, p.n_tiles, p.causal && !p.kv_len && !p.q_len, &slot, &rank);
-  *bh = head_of_slot(slot, heads / (int)p.H, (int)p.H);
+  *bh = slot;
+  if (p.kv_len || p.q_len) *bh = head_of_slot(slot, heads / (int)p.H, (int)p.H, true);
   return rank;
 }
 

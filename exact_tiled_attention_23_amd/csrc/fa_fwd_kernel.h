@@ -105,11 +105,12 @@ __device__ __forceinline__ int xcd_unit(int bid, int64_t n_units) {
 }
 
 // (b, h) of head slot `slot` (slots are the consecutive runs of units that one head's tiles
-// occupy). Slots run over the batch fastest, so the run of slots an XCD takes holds heads of
-// every batch element: with per-batch key padding the work of an element varies, and a slot
-// order by batch would give whole elements, and so unequal work, to single XCDs.
-__device__ __forceinline__ int head_of_slot(int slot, int B, int H) {
-  return (slot % B) * H + slot / B;
+// occupy). With per-batch padding (`mixed`) the work of a batch element varies, and slots in
+// (b, h) order would give whole elements, and so unequal work, to single XCDs; the slots then
+// run over the batch fastest, so the run of slots an XCD takes holds heads of every element.
+// Without padding they keep the (b, h) order, which reads K and V from fewer memory regions.
+__device__ __forceinline__ int head_of_slot(int slot, int B, int H, bool mixed) {
+  return mixed ? (slot % B) * H + slot / B : slot;
 }
 
 // Work unit -> (bh, query tile, split); causal runs the longest query tiles first.
@@ -148,7 +149,8 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   const int per_head = p.n_qtiles * ns;
   int slot, rem;
   unit_slot(bid, p.n_units, (int)p.BH, per_head, p.causal && !p.kv_len && !p.q_len, &slot, &rem);
-  u.bh = head_of_slot(slot, (int)(p.BH / p.H), (int)p.H);
+  u.bh = slot;
+  if (p.kv_len || p.q_len) u.bh = head_of_slot(slot, (int)p.BH / (int)p.H, (int)p.H, true);  // B*H < 2^31
   u.qt = rem / ns;
   u.split = rem % ns;
   if (p.causal) u.qt = p.n_qtiles - 1 - u.qt;
