@@ -41,6 +41,9 @@
 
 namespace fa {
 
+// A compile-time integer passed as a value (selects an unrolled copy of a loop body).
+template <int V> struct Int { static constexpr int value = V; };
+
 // Reference maximum may lag the true row maximum by up to this much (base-2 units).
 constexpr float kRescaleSlack = 8.0f;
 
@@ -49,9 +52,14 @@ typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Maximum of x over the lane pair (i, i ^ 32). The two swapped values are plain lane moves of
+// a maximum already formed in this kernel, so they need no canonicalisation: the final max is
+// written as one instruction (fmaxf would first quiet each operand with a max of itself).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -203,7 +211,8 @@ void fwd16_kernel(FwdParams p) {
     ld_vok[i] = cv < VCH;
   }
 
-  auto issue_tile = [&](int j0, int buf) {
+  auto issue_tile = [&](int j0, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     const unsigned char* kt = Kh + (int64_t)j0 * ksnb;
     const unsigned char* vt = Vh + (int64_t)j0 * vsnb;
     unsigned char* kb = lds + buf * 2 * TILEB;
@@ -263,12 +272,14 @@ void fwd16_kernel(FwdParams p) {
   float lsum = 0.f;        // this lane half's share of the denominator
   const float c = p.scale_log2;
 
-  // Tile t lives in buffer (t - t_lo) & 1 and is copied one tile ahead.
-  if (t_lo < t_hi) issue_tile(t_lo * BC, 0);
+  // Tile t lives in buffer (t - t_lo) & 1 and is copied one tile ahead. The loop below runs
+  // two tiles per iteration, one per buffer, so the buffer is a compile-time constant in each
+  // copy of the body and every LDS address is a per-lane register plus an immediate offset.
+  if (t_lo < t_hi) issue_tile(t_lo * BC, Int<0>{});
 
-  for (int t = t_lo; t < t_hi; ++t) {
+  auto tile_step = [&](const int t, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     const int j0 = t * BC;
-    const int buf = (t - t_lo) & 1;
     const unsigned char* kb = lds + buf * 2 * TILEB;
     const unsigned char* vb = kb + TILEB;
     wait_vmem();  // this wave's copies of tile t have landed
@@ -284,7 +295,7 @@ void fwd16_kernel(FwdParams p) {
       }
     }
     __syncthreads();  // tile t visible to all waves; all waves are done with tile t-1
-    if (t + 1 < t_hi) issue_tile(j0 + BC, buf ^ 1);
+    if (t + 1 < t_hi) issue_tile(j0 + BC, Int<buf ^ 1>{});
 
     if (j0 < wave_hi) {
       // ---- S^T = K . Q^T. The sub-tiles' products advance together, one reduction step
@@ -349,7 +360,7 @@ void fwd16_kernel(FwdParams p) {
         mx = pair_max(mx);
         // Move the reference when some row's maximum rose more than the slack above it,
         // or when a row sees its first valid key (its reference is still -inf).
-        if (__any(mx > kRescaleSlack || (mref == -INFINITY && mx != -INFINITY))) {
+        if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
           const float mnew = fmaxf(mref, mx + muse);
           if (mnew != mref) {
             const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
@@ -377,9 +388,11 @@ void fwd16_kernel(FwdParams p) {
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
             va[h][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-        float a0 = 0.f, a1 = 0.f;
+        x[0] = __builtin_amdgcn_exp2f(x[0]);
+        x[1] = __builtin_amdgcn_exp2f(x[1]);
+        float a0 = x[0], a1 = x[1];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
+        for (int i = 2; i < 16; i += 2) {
           x[i] = __builtin_amdgcn_exp2f(x[i]);
           x[i + 1] = __builtin_amdgcn_exp2f(x[i + 1]);
           a0 += x[i];
@@ -398,6 +411,11 @@ void fwd16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
       }
     }
+  };
+  for (int t = t_lo; t < t_hi; t += 2) {
+    tile_step(t, Int<0>{});
+    if (t + 1 >= t_hi) break;
+    tile_step(t + 1, Int<1>{});
   }
 
   // ---- epilogue
