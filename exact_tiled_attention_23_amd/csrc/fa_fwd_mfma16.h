@@ -268,7 +268,7 @@ void fwd16_kernel(FwdParams p) {
 #pragma unroll
   for (int t = 0; t < NDT; ++t) oacc[t] = f32x16{};
   float mref = -INFINITY;  // reference maximum (scaled base-2 logits)
-  float muse = 0.f;        // mref, or 0 while mref is -inf (no valid key seen yet)
+  float nmuse = 0.f;       // -mref, or 0 while mref is -inf (no valid key seen yet): the FMA addend
   float lsum = 0.f;        // this lane half's share of the denominator
   const float c = p.scale_log2;
 
@@ -350,18 +350,21 @@ void fwd16_kernel(FwdParams p) {
       // run while the matrix core works on another.
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        // x = s*c - m_use is the exponent of p against the current reference; its row
-        // maximum decides whether the reference has to move.
+        // x = s*c - mref (s*c while mref is -inf) is the exponent of p against the current
+        // reference; its row maximum decides whether the reference has to move.
         float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(s[u][i], c, -muse);
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11])), fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]))));
+        for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(s[u][i], c, nmuse);
+        // Sixteen values in eight three-input maxima (each nested pair below becomes one v_max3).
+        float m3[5];
+#pragma unroll
+        for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
+        float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), x[15]));
         mx = pair_max(mx);
         // Move the reference when some row's maximum rose more than the slack above it,
         // or when a row sees its first valid key (its reference is still -inf).
         if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
-          const float mnew = fmaxf(mref, mx + muse);
+          const float mnew = fmaxf(mref, mx - nmuse);
           if (mnew != mref) {
             const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
             lsum *= alpha;
@@ -369,11 +372,11 @@ void fwd16_kernel(FwdParams p) {
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
               for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            const float delta = mnew - muse;
+            const float delta = mnew + nmuse;
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] -= delta;
             mref = mnew;
-            muse = mnew;
+            nmuse = -mnew;
           }
         }
         // V^T fragments of this sub-tile, read before the exponentials so the reads land
