@@ -267,9 +267,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
   if (ntiles > 0) issue(0, 0);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Two tiles per iteration, one per buffer: the buffer is a compile-time constant in each copy
+  // of the body, so LDS addresses are per-lane registers plus immediate offsets.
+  auto tile_step = [&](const int t, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     const int j0 = t * BC;
-    const int buf = t & 1;
     unsigned char* kb = lds + buf * 2 * TILEB;
     unsigned char* vb = kb + TILEB;
     wait_vmem();
@@ -351,6 +353,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::run(kt[h][dt], dsf[h], acc[dt]);
       }
     }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, Int<0>{});
+    if (t + 1 >= ntiles) break;
+    tile_step(t + 1, Int<1>{});
   }
 
   // ---- dQ = scale * acc; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.
@@ -466,9 +473,11 @@ void bwd_dkdv_kernel(BwdParams p) {
   };
   if (t0 < nqt) issue(t0, 0);
 
-  for (int t = t0; t < nqt; ++t) {
+  // Two query tiles per iteration, one per buffer (compile-time buffer offsets, as in the dQ
+  // kernel).
+  auto tile_step = [&](const int t, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     const int i0 = t * BQ;
-    const int buf = (t - t0) & 1;
     const unsigned char* qb = lds + buf * BUFB;
     const unsigned char* ob = qb + TILEB;
     const float* sb = reinterpret_cast<const float*>(qb + 2 * TILEB);
@@ -565,6 +574,11 @@ void bwd_dkdv_kernel(BwdParams p) {
           dka[dt] = M::run(tq[h][dt], dsf[h], dka[dt]);
         }
     }
+  };
+  for (int t = t0; t < nqt; t += 2) {
+    tile_step(t, Int<0>{});
+    if (t + 1 >= nqt) break;
+    tile_step(t + 1, Int<1>{});
   }
 
   // ---- dK = scale * dka, dV = dva; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.

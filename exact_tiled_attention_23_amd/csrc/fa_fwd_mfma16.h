@@ -81,8 +81,10 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(const void* base, unsigned off, unsigned lds_addr) {
+  // The destination is wave-uniform; readfirstlane keeps it in a scalar register even where the
+  // compiler has a copy of the value in a vector register (it may otherwise pick that one).
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-               :: "v"(off), "s"(lds_addr), "s"(base) : "memory", "m0");
+               :: "v"(off), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
