@@ -19,8 +19,9 @@
 //    and denominator are rescaled by 2^(m_old - m_new) only when some row's maximum
 //    rises more than kRescaleSlack above the reference (a wave-uniform branch). Until
 //    then probabilities are formed against the stale reference and stay <= 2^slack.
-//    The exponent s*c - m is formed first and its row maximum taken afterwards, so the
-//    usual case costs one FMA, half a max and one exp2 per score.
+//    The exponent s*c - m is formed first and its row maximum over the whole key tile
+//    taken afterwards (one decision per tile), so the usual case costs one FMA, half a
+//    max and one exp2 per score.
 //    The final O = acc / l is the same quotient whichever reference is used, so the
 //    result is exact up to rounding ("Paper: FlashAttention", Objectives: the
 //    online-softmax state is defined up to a common rescaling).
@@ -347,42 +348,59 @@ void fwd16_kernel(FwdParams p) {
             if (32 * u + 16 * (i / 8) + (i % 8) >= lim) s[u][i] = -INFINITY;
       }
 
-      // ---- online softmax and O^T += V^T . P^T, one 32-key sub-tile at a time (each
-      // sub-tile is one step of the recurrence), so the vector work on one sub-tile can
-      // run while the matrix core works on another.
+      // ---- online softmax: the exponents x = s*c - mref of the whole tile (s*c while mref is
+      // -inf), and one decision per tile on moving the reference, from the row maximum over
+      // all of the tile's keys.
+      float x[NSUB][16];
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) {
-        // x = s*c - mref (s*c while mref is -inf) is the exponent of p against the current
-        // reference; its row maximum decides whether the reference has to move.
-        float x[16];
+      for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(s[u][i], c, nmuse);
-        // Sixteen values in eight three-input maxima (each nested pair below becomes one v_max3).
-        float m3[5];
+        for (int i = 0; i < 16; ++i) x[u][i] = __builtin_fmaf(s[u][i], c, nmuse);
+      float mx;
+      {
+        // 16*NSUB values in three-input maxima (each nested pair below becomes one v_max3).
+        constexpr int NV = 16 * NSUB;
+        float m[NV];
 #pragma unroll
-        for (int k = 0; k < 5; ++k) m3[k] = fmaxf(fmaxf(x[3 * k], x[3 * k + 1]), x[3 * k + 2]);
-        float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), x[15]));
-        mx = pair_max(mx);
-        // Move the reference when some row's maximum rose more than the slack above it,
-        // or when a row sees its first valid key (its reference is still -inf).
-        if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
-          const float mnew = fmaxf(mref, mx - nmuse);
-          if (mnew != mref) {
-            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
-            lsum *= alpha;
+        for (int i = 0; i < NV; ++i) m[i] = x[i / 16][i % 16];
+        int cnt = NV;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+        for (int lvl = 0; lvl < 6; ++lvl) {
+          if (cnt > 1) {
+            int o = 0, i = 0;
 #pragma unroll
-              for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            const float delta = mnew + nmuse;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] -= delta;
-            mref = mnew;
-            nmuse = -mnew;
+            for (; i + 2 < cnt; i += 3) m[o++] = fmaxf(fmaxf(m[i], m[i + 1]), m[i + 2]);
+            if (cnt - i == 2) m[o++] = fmaxf(m[i], m[i + 1]);
+            else if (cnt - i == 1) m[o++] = m[i];
+            cnt = o;
           }
         }
-        // V^T fragments of this sub-tile, read before the exponentials so the reads land
-        // while they run (order pinned below).
+        mx = pair_max(m[0]);
+      }
+      // Move the reference when some row's maximum rose more than the slack above it, or when
+      // a row sees its first valid key (its reference is still -inf).
+      if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
+        const float mnew = fmaxf(mref, mx - nmuse);
+        if (mnew != mref) {
+          const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
+          lsum *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+          const float delta = mnew + nmuse;
+#pragma unroll
+          for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[u][i] -= delta;
+          mref = mnew;
+          nmuse = -mnew;
+        }
+      }
+      // ---- probabilities and O^T += V^T . P^T, one 32-key sub-tile at a time, so the
+      // vector work on one sub-tile can run while the matrix core works on another.
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
         frag va[2][NDT];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -393,22 +411,22 @@ void fwd16_kernel(FwdParams p) {
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
             va[h][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           }
-        x[0] = __builtin_amdgcn_exp2f(x[0]);
-        x[1] = __builtin_amdgcn_exp2f(x[1]);
-        float a0 = x[0], a1 = x[1];
+        x[u][0] = __builtin_amdgcn_exp2f(x[u][0]);
+        x[u][1] = __builtin_amdgcn_exp2f(x[u][1]);
+        float a0 = x[u][0], a1 = x[u][1];
 #pragma unroll
         for (int i = 2; i < 16; i += 2) {
-          x[i] = __builtin_amdgcn_exp2f(x[i]);
-          x[i + 1] = __builtin_amdgcn_exp2f(x[i + 1]);
-          a0 += x[i];
-          a1 += x[i + 1];
+          x[u][i] = __builtin_amdgcn_exp2f(x[u][i]);
+          x[u][i + 1] = __builtin_amdgcn_exp2f(x[u][i + 1]);
+          a0 += x[u][i];
+          a1 += x[u][i + 1];
         }
         lsum += a0 + a1;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           frag pf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (T)x[8 * h + e];
+          for (int e = 0; e < 8; ++e) pf[e] = (T)x[u][8 * h + e];
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::run(va[h][dt], pf, oacc[dt]);
         }
