@@ -167,6 +167,32 @@ def test_large_negative_logits(dtype, causal):
     compare(o, lse, ro, rl, dtype, "large negative logits")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_and_jumping_logits(dtype, D, causal):
+    """Row maxima that keep rising along the keys (Q[..., -1] = 1, K[j, -1] = 2j: the scaled
+    base-2 logit grows by 0.26-0.36 per key, 14-24 per 64-key tile, above the reference's
+    slack of 8), so the reference maximum has to move at every key tile; and a single key
+    whose logit stands 27-38 base-2 units above the rest, in the second half of a 64-key
+    tile (key 100), so it moves on a key that sits late in its tile. Both against the oracle."""
+    N = 300
+    say(f"rising and jumping logits dtype={dtype} D={D} causal={causal}")
+    x = generate(1, 2, N, D, dtype, causal=causal, seed=87)
+    x.q[..., -1] = 1.0
+    x.k[..., -1] = 2.0 * torch.arange(N, dtype=torch.float32).to(x.k.dtype)
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+    compare(o, lse, ro, rl, dtype, "rising logits")
+    x = generate(1, 2, N, D, dtype, causal=causal, seed=88)
+    x.q[..., -1] = 4.0
+    x.k[..., -1] = 0.0
+    x.k[:, :, 100, -1] = 60.0
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+    compare(o, lse, ro, rl, dtype, "jumping logit")
+
+
 def test_deterministic():
     """No atomics: two runs are bitwise identical."""
     say("determinism bf16 N=1000")
