@@ -241,6 +241,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
   const float delta = pair_sum(dsum);
+  constexpr bool kDeltaInAcc = D <= 64;
+  f32x16 ndelta16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndelta16[i] = -delta;
   const float lse = qrow < nq ? p.lse[(int64_t)bh * n + qrow] : -INFINITY;
   // P = 2^(s*c - mo): +inf offset for a row with no valid key (its P is 0).
   const float mo = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
@@ -293,7 +297,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // S^T and dP^T for 32 keys (rows of K and V in the permuted order a_row_key), with the
         // row fragments of step st+PD and the K^T transpose fragments of the dQ product below
         // read while step st's products run (order pinned as in the dK/dV kernel).
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // At D <= 64 the dP^T accumulator starts at -Delta (this lane's query), so the products
+        // leave dP - Delta in it and dS needs one multiply; at D >= 96 the 16 registers that
+        // takes are not free, and Delta is subtracted per element instead.
+        f32x16 s = f32x16{}, dp = kDeltaInAcc ? ndelta16 : f32x16{};
         // At D = 128 only the first half of the K^T fragments is read ahead (all of them would
         // not fit in the registers of two waves per SIMD); the second half is read while the
         // first half's products run.
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int i = 0; i < 16; ++i) {
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo));
           x = (edge && 32 * u + 16 * (i / 8) + (i % 8) >= lim) ? 0.f : x;
-          ds[i] = x * (dp[i] - delta);
+          ds[i] = kDeltaInAcc ? x * dp[i] : x * (dp[i] - delta);
         }
         frag dsf[2];
 #pragma unroll
