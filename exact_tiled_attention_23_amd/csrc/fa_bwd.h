@@ -22,7 +22,7 @@
 //    formed per lane and feed dQ^T = K^T.dS^T straight from the accumulator registers, with
 //    K^T fragments from transpose reads (ds_read_b64_tr_b16). Its prologue also forms
 //    Delta = rowsum(dO o O) and stores, per 64-row block, the rows' exponent offsets
-//    (LSE log2 e, +inf for a row with no key or past N) next to their Delta values.
+//    (LSE log2 e, +inf for a row with no key or past N) next to their negated Delta values.
 //  * bwd_dkdv_kernel: one workgroup per (batch, head, key tile), each wave 32 keys held in
 //    registers; it walks the query tiles. S = Q.K^T and dP = dO.V^T give each lane one key
 //    and 16 queries of every 32-query sub-tile (Q and dO rows are read in a permuted order so
@@ -61,7 +61,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   Strides3 st_q, st_k, st_v, st_o, st_do, st_dq, st_dk, st_dv;
-  float* stats;       // [B*H][ceil(N/64)][128] floats: 64 exponent offsets, then 64 Delta values
+  float* stats;       // [B*H][ceil(N/64)][128] floats: 64 exponent offsets, then 64 values of -Delta
   const int32_t* kv_len;  // nullable: keys at or past kv_len[b] are padding
   const int32_t* q_len;   // nullable: query rows at or past q_len[b] are padding (not read, dQ = 0)
   int64_t H, N;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (g == 0 && qrow < n64 * kStatRows) {
       float* st = p.stats + ((int64_t)bh * n64 + qrow / kStatRows) * (2 * kStatRows) + qrow % kStatRows;
       st[0] = mo;
-      st[kStatRows] = qrow < n ? delta : 0.f;
+      st[kStatRows] = qrow < n ? -delta : 0.f;
     }
   }
 
@@ -468,7 +468,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     dva[t] = f32x16{};
   }
   const float c = p.scale_log2;
-  // Stats copy: lanes 0-31 bring the 512-byte block of 64 offsets and 64 Delta values,
+  // Stats copy: lanes 0-31 bring the 512-byte block of 64 offsets and 64 values of -Delta,
   // lanes 32-63 the same bytes again (the copy instruction always moves 1 KB).
   const unsigned stat_off = (unsigned)(lane & 31) * 16;
 
@@ -506,7 +506,21 @@ void bwd_dkdv_kernel(BwdParams p) {
       // fragments of the dV/dK products below are read in the same stretch, so no product
       // waits on a read issued just before it. The order is pinned with scheduling-group
       // barriers (the scheduler otherwise places each read right before its product).
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key. The dP
+      // accumulator starts at those queries' -Delta, so the products leave dP - Delta in it.
+      float mo[16];
+      f32x16 dp;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4* pm = reinterpret_cast<const float4*>(sb + 32 * u + 16 * h + 8 * g);
+        const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * u + 16 * h + 8 * g);
+        const float4 m0 = pm[0], m1 = pm[1], d0 = pd[0], d1 = pd[1];
+        mo[8 * h + 0] = m0.x; mo[8 * h + 1] = m0.y; mo[8 * h + 2] = m0.z; mo[8 * h + 3] = m0.w;
+        mo[8 * h + 4] = m1.x; mo[8 * h + 5] = m1.y; mo[8 * h + 6] = m1.z; mo[8 * h + 7] = m1.w;
+        dp[8 * h + 0] = d0.x; dp[8 * h + 1] = d0.y; dp[8 * h + 2] = d0.z; dp[8 * h + 3] = d0.w;
+        dp[8 * h + 4] = d1.x; dp[8 * h + 5] = d1.y; dp[8 * h + 6] = d1.z; dp[8 * h + 7] = d1.w;
+      }
+      f32x16 s = f32x16{};
       frag tq[2][NDT], to[2][NDT];
       {
         constexpr int PD = 2;
@@ -542,18 +556,6 @@ void bwd_dkdv_kernel(BwdParams p) {
           __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                    // transpose reads
         }
       }
-      // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key.
-      float mo[16], dl[16];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float4* pm = reinterpret_cast<const float4*>(sb + 32 * u + 16 * h + 8 * g);
-        const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * u + 16 * h + 8 * g);
-        const float4 m0 = pm[0], m1 = pm[1], d0 = pd[0], d1 = pd[1];
-        mo[8 * h + 0] = m0.x; mo[8 * h + 1] = m0.y; mo[8 * h + 2] = m0.z; mo[8 * h + 3] = m0.w;
-        mo[8 * h + 4] = m1.x; mo[8 * h + 5] = m1.y; mo[8 * h + 6] = m1.z; mo[8 * h + 7] = m1.w;
-        dl[8 * h + 0] = d0.x; dl[8 * h + 1] = d0.y; dl[8 * h + 2] = d0.z; dl[8 * h + 3] = d0.w;
-        dl[8 * h + 4] = d1.x; dl[8 * h + 5] = d1.y; dl[8 * h + 6] = d1.z; dl[8 * h + 7] = d1.w;
-      }
       const bool diag = p.causal && qs < kw + 31;
       float pr[16], ds[16];
 #pragma unroll
@@ -562,7 +564,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
         x = dead ? 0.f : x;
         pr[i] = x;
-        ds[i] = x * (dp[i] - dl[i]);
+        ds[i] = x * dp[i];
       }
       frag pf[2], dsf[2];
 #pragma unroll
@@ -781,7 +783,7 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
       const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
       x = dead ? 0.f : x;
       pf[i / 8][i % 8] = (T)x;
-      dsf[i / 8][i % 8] = (T)(x * (dp[i] - dl[i]));
+      dsf[i / 8][i % 8] = (T)(x * (dp[i] + dl[i]));  // dl holds -Delta
     }
     // dV^T += dO^T . P and dK^T += Q^T . dS, reading pair j+1 while pair j's products run.
 #pragma unroll

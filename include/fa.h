@@ -178,7 +178,7 @@ int fa_merge_states(const float* part_o, const float* part_lse, int n_states,
 
 /*
  * fa_bwd_workspace_bytes - device workspace fa_bwd needs: B*H*ceil(N/64)*128 float32 (per
- * 64-row block of each (b, h): the rows' exponent offsets, then their Delta values). 0 when any
+ * 64-row block of each (b, h): the rows' exponent offsets, then their negated Delta values). 0 when any
  * size is 0, -1 for a negative size or a byte count that overflows. Pure host arithmetic.
  */
 int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
