@@ -16,7 +16,7 @@ The GPU parity tests check the kernels themselves; this pins the layout arithmet
 import pytest
 
 # (D, key tile BC, waves NW) of the forward kernel per head dimension
-FWD_SHAPES = [(32, 128, 4), (64, 128, 4), (96, 64, 8), (128, 64, 8), (256, 64, 4)]
+FWD_SHAPES = [(32, 128, 4), (64, 64, 4), (96, 64, 8), (128, 64, 8), (256, 64, 4), (96, 64, 4), (128, 64, 4)]
 # (D, tile rows, waves) of the backward's tile plans: dQ kernel K/V tiles, dK/dV Q/dO tiles, and
 # the LDS dK/dV kernel's K/V and Q/dO tiles (D = 96, 128)
 BWD_PLANS = [(32, 64, 4), (64, 64, 4), (96, 64, 4), (128, 64, 4), (96, 128, 8), (96, 64, 8),
