@@ -163,10 +163,13 @@ __device__ __forceinline__ typename Mma<T>::frag tr_frag(const unsigned char* t,
   return __builtin_bit_cast(typename Mma<T>::frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+template <int D> constexpr int dkdv_waves_per_eu() { return D >= 128 ? 1 : (D <= 32 ? 3 : 2); }
+template <int D> constexpr int dq_waves_per_eu() { return D <= 32 ? 3 : 2; }
+
 // ------------------------------------------------------------------------------------------
 // dQ (and Delta, exponent offsets): one workgroup per (b, h, query tile of 32*NW rows).
 template <typename T, int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D>(), dq_waves_per_eu<D>()))) void bwd_dq_kernel(BwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   static_assert(sizeof(T) == 2, "16-bit element types only");
@@ -385,7 +388,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // dK, dV: one workgroup per (b, h, key tile of 32*NW keys); query tiles of BQ rows.
 // Two waves per SIMD where the registers allow it; at D = 128 the K, V fragments and the dK, dV
 // accumulators alone take 192 registers, so one.
-template <int D> constexpr int dkdv_waves_per_eu() { return D >= 128 ? 1 : 2; }
 
 template <typename T, int D, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64)
