@@ -4,7 +4,8 @@ Thirty configurations drawn once from a fixed seed cover combinations that the h
 cases do not name: B, H, ragged N up to 700, every head dimension, both 16-bit types (and
 float32 for the forward), causal or not, key padding with random kv_len (0 included), and a
 random part count for the split. Twenty more, from a second seed, add query padding (random
-q_len, with NaN in the padding rows of Q and dO). Tolerances are the ones of the dedicated tests.
+q_len, with NaN in the padding rows of Q and dO), and forty more come from a third seed.
+Tolerances are the ones of the dedicated tests.
 """
 
 import numpy as np
@@ -41,7 +42,8 @@ def draw_configs(count=30, seed=2024, query_padding=False):
     return out
 
 
-CONFIGS = draw_configs() + [(100 + c[0],) + c[1:] for c in draw_configs(20, seed=77, query_padding=True)]
+CONFIGS = (draw_configs() + [(100 + c[0],) + c[1:] for c in draw_configs(20, seed=77, query_padding=True)]
+           + [(200 + c[0],) + c[1:] for c in draw_configs(40, seed=31337)])
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"c{c[0]}")
