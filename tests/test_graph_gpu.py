@@ -20,8 +20,9 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def test_forward_split_backward_in_graph():
-    B, H, N, D = 1, 4, 1000, 128
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_split_backward_in_graph(D):
+    B, H, N = 1, 4, 1000
     x = generate(B, H, N, D, "bf16", causal=True, seed=301)
     q, k, v = (t.to(DEV) for t in (x.q, x.k, x.v))
     do = generate_grad_output(B, H, N, D, "bf16", seed=302).to(DEV)
@@ -44,7 +45,7 @@ def test_forward_split_backward_in_graph():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    say("capturing forward + split forward + backward")
+    say(f"capturing forward + split forward + backward, D={D}")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
