@@ -574,11 +574,13 @@ void bwd_dkdv_kernel(BwdParams p) {
       // Masks only where a key of the wave is padding or the tile meets the diagonal (a
       // wave-uniform test); elsewhere every (query, key) pair is live.
       if (diag || any_key_dead) {
+        // Element i (query qs + 16(i/8) + 8g + i%8) is dead when its offset 16(i/8) + i%8 is
+        // below lim: always for a padding key, never off the diagonal.
+        const int lim = key_dead ? INT_MAX : (diag ? key - qs - 8 * g : INT_MIN);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
-          const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
-          x = dead ? 0.f : x;
+          x = (16 * (i / 8) + (i % 8) < lim) ? 0.f : x;
           pr[i] = x;
           ds[i] = x * dp[i];
         }
@@ -806,11 +808,13 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
     // copy of this code pushes the kernel past its registers (spills measured 3% slower), so
     // there the masked form runs on every tile.
     if (D >= 128 || diag || any_key_dead) {
+      // Element i (query qs + 16(i/8) + 8g + i%8) is dead when its offset 16(i/8) + i%8 is below
+      // lim: always for a padding key, never off the diagonal.
+      const int lim = key_dead ? INT_MAX : (diag ? key - qs - 8 * g : INT_MIN);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
-        const bool dead = key_dead || (diag && qs + 16 * (i / 8) + 8 * g + (i % 8) < key);
-        x = dead ? 0.f : x;
+        x = (16 * (i / 8) + (i % 8) < lim) ? 0.f : x;
         pf[i / 8][i % 8] = (T)x;
         dsf[i / 8][i % 8] = (T)(x * (dp[i] + dl[i]));  // dl holds -Delta
       }
