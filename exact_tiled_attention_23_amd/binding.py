@@ -159,6 +159,28 @@ def _stream_handle(stream, dev):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _side_stream(stream, dev):
+    """The launch stream as a torch stream when it is not the current stream of `dev`, else None.
+
+    Temporaries made here come from the caching allocator on the current stream. When the
+    kernels run on another stream, each such tensor is marked as used there (record_stream), so
+    its memory is not handed to a later allocation before that stream has passed the kernels."""
+    if stream is None:
+        return None
+    if not isinstance(stream, torch.cuda.Stream):
+        h = int(stream)
+        stream = torch.cuda.default_stream(dev) if h == 0 else torch.cuda.ExternalStream(h, device=dev)
+    cur = torch.cuda.current_stream(dev)
+    return None if stream.cuda_stream == cur.cuda_stream else stream
+
+
+def _mark_used_on(side, *tensors):
+    if side is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(side)
+
+
 def _lengths_device(lens, B, N, dev, what):
     """Per-batch lengths (kv_len or q_len) as a device int32 tensor [B], or None."""
     if lens is None:
@@ -213,16 +235,20 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, q_len=None, out=No
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
     dev = q.device
+    made = []  # tensors allocated here (on the current stream)
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        made.append(lse)
     if out.shape != q.shape or out.dtype != q.dtype or (out.stride(3) != 1 and D > 1):
         raise ValueError("out must be shaped and typed like q, with a contiguous head dimension")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N]")
     kv_dev = _lengths_device(kv_len, B, N, dev, "kv_len")
     q_dev = _lengths_device(q_len, B, N, dev, "q_len")
+    made += [t for t, given in ((kv_dev, kv_len), (q_dev, q_len)) if t is not None and t is not given]
     handle = _stream_handle(stream, dev)
     strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, strides,
@@ -239,11 +265,13 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, q_len=None, out=No
                 raise ValueError(f"n_splits must lie in [1, {MAX_SPLITS}] (got {n_splits})")
             if workspace is None:
                 workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                made.append(workspace)
             if not workspace.is_cuda or not workspace.is_contiguous():
                 raise ValueError("workspace must be a contiguous device tensor")
             ws_bytes = workspace.numel() * workspace.element_size()
             rc = fa_fwd_split(*args, n_splits, workspace.data_ptr(), ws_bytes, handle)
     _check(rc)
+    _mark_used_on(_side_stream(stream, dev), *made)
     return out, lse
 
 
@@ -261,10 +289,13 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
     dtype = torch.float32 if dtype is None else dtype
     if dtype not in _TORCH_DTYPE:
         raise TypeError("dtype must be float32, bfloat16 or float16")
+    made = []
     if out is None:
         out = torch.empty((B, H, N, D), dtype=dtype, device=dev)
+        made.append(out)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        made.append(lse)
     if out.shape != (B, H, N, D) or out.dtype != dtype or (out.stride(3) != 1 and D > 1):
         raise ValueError("out must be [B, H, N, D] of dtype with a contiguous last dimension")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -273,6 +304,7 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
         rc = fa_merge_states(part_o.data_ptr(), part_lse.data_ptr(), S, B, H, N, D, out.data_ptr(),
                              list(out.stride()[:3]), lse.data_ptr(), _TORCH_DTYPE[dtype], _stream_handle(stream, dev))
     _check(rc)
+    _mark_used_on(_side_stream(stream, dev), *made)
     return out, lse
 
 
@@ -299,9 +331,16 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, q_len
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
     dev = q.device
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    made = []  # tensors allocated here (on the current stream)
+    if dq is None:
+        dq = torch.empty_like(q)
+        made.append(dq)
+    if dk is None:
+        dk = torch.empty_like(q)
+        made.append(dk)
+    if dv is None:
+        dv = torch.empty_like(q)
+        made.append(dv)
     for t in (dq, dk, dv):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or (t.stride(3) != 1 and t.shape[3] > 1):
             raise ValueError("dq, dk, dv must be device tensors shaped and typed like q, last dimension contiguous")
@@ -310,10 +349,12 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, q_len
         raise ValueError("sizes too large")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     kv_dev = _lengths_device(kv_len, B, N, dev, "kv_len")
     q_dev = _lengths_device(q_len, B, N, dev, "q_len")
+    made += [t for t, given in ((kv_dev, kv_len), (q_dev, q_len)) if t is not None and t is not given]
     every = (q, k, v, o, do, dq, dk, dv)
     strides = None if all(t.is_contiguous() for t in every) else [x for t in every for x in t.stride()[:3]]
     with torch.cuda.device(dev):
@@ -323,6 +364,7 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, q_len
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream_handle(stream, dev))
     _check(rc)
+    _mark_used_on(_side_stream(stream, dev), *made)
     return dq, dk, dv
 
 

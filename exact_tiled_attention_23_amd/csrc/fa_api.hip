@@ -253,7 +253,7 @@ extern "C" const char* fa_strerror(int code) {
     case FA_ERR_SHAPE: return "invalid sizes (negative, or too large for the kernel's indexing)";
     case FA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension (forward: f32, bf16, f16 with D 32, 64, 96, 128, and 256 for bf16/f16; backward: bf16, f16 with D 32, 64, 96, 128)";
     case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE, q_len and kv_len 4 bytes)";
-    case FA_ERR_ARG: return "invalid argument (scale finite and > 0, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
+    case FA_ERR_ARG: return "invalid argument (scale finite, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown error code";
   }
@@ -270,7 +270,7 @@ int validate_forward(const void* Q, const void* K, const void* V, void* O, float
   if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
   if (!supported(dtype, D)) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;
@@ -472,7 +472,7 @@ int bwd_precheck(int64_t B, int64_t H, int64_t N, int64_t D, float scale, int ca
   if (B < 0 || H < 0 || N < 0 || D < 0) return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_UNSUPPORTED;
   if (!bwd_supported(dtype, D)) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;

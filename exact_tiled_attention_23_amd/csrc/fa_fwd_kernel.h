@@ -79,7 +79,7 @@ struct FwdParams {
   int64_t o_sb, o_sh, o_sn;
   int64_t H;
   int64_t N;
-  float scale_log2;       // scale * log2(e), > 0
+  float scale_log2;       // scale * log2(e), any finite value
   int causal;
   int n_qtiles;           // ceil(N / BR)
   int64_t n_units;        // B * H * n_qtiles * n_splits (the grid size)
@@ -351,28 +351,25 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
         }
       }
 
-      // ---- masks: only where the tile crosses the kv_len edge or this wave's diagonal
+      // ---- masks: only where the tile crosses the kv_len edge or this wave's diagonal. A dead
+      // key's scaled logit is -inf and its probability 0, for a scale of either sign (or zero).
       const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq;
-      if (need_mask) {
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t key = j0 + 32 * u + acc_key<KPER>(i, g);
-            const bool dead = key >= kvl || (p.causal && key > qrow) || qrow >= nq;
-            if (dead) s[u][i] = -INFINITY;
-          }
-        }
-      }
+      auto dead = [&](int u, int i) __attribute__((always_inline)) {
+        const int64_t key = j0 + 32 * u + acc_key<KPER>(i, g);
+        return key >= kvl || (p.causal && key > qrow) || qrow >= nq;
+      };
 
-      // ---- online softmax (base 2)
+      // ---- online softmax (base 2): running max of the scaled logits s*c
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[u][i]);
+        for (int i = 0; i < 16; ++i) {
+          const float x = (need_mask && dead(u, i)) ? -INFINITY : s[u][i] * c;
+          mx = fmaxf(mx, x);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m2, mx * c);
+      const float m_new = fmaxf(m2, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
       m2 = m_new;
@@ -385,7 +382,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][i], c, -m_use));
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][i], c, -m_use));
+          if (need_mask && dead(u, i)) pv = 0.f;
           s[u][i] = pv;
           lsum += pv;
         }

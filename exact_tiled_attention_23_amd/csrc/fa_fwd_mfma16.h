@@ -334,20 +334,6 @@ void fwd16_kernel(FwdParams p) {
         }
       }
 
-      // ---- masks (edge tiles, and every tile of the wave that holds the last query rows
-      // before padding): key j0 + 32u + acc_key(i, g) is dead when it is at or past kv_len,
-      // or (causal) after this lane's query, or this lane's query is padding.
-      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq) {
-        int lim = qrow < nq ? kvl - j0 : 0;
-        if (p.causal) lim = min(lim, qrow - j0 + 1);
-        lim -= 8 * g;
-#pragma unroll
-        for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * u + 16 * (i / 8) + (i % 8) >= lim) s[u][i] = -INFINITY;
-      }
-
       // ---- online softmax: the exponents x = s*c - mref of the whole tile (s*c while mref is
       // -inf), and one decision per tile on moving the reference, from the row maximum over
       // all of the tile's keys.
@@ -356,6 +342,22 @@ void fwd16_kernel(FwdParams p) {
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[u][i] = __builtin_fmaf(s[u][i], c, nmuse);
+
+      // ---- masks (edge tiles, and every tile of the wave that holds the last query rows
+      // before padding): key j0 + 32u + acc_key(i, g) is dead when it is at or past kv_len,
+      // or (causal) after this lane's query, or this lane's query is padding. The exponent is
+      // set to -inf after the scaling, so the mask holds for a scale of either sign (or zero)
+      // and whatever a padding key's score holds.
+      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq) {
+        int lim = qrow < nq ? kvl - j0 : 0;
+        if (p.causal) lim = min(lim, qrow - j0 + 1);
+        lim -= 8 * g;
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * u + 16 * (i / 8) + (i % 8) >= lim) x[u][i] = -INFINITY;
+      }
       float mx;
       {
         // 16*NSUB values in three-input maxima (each nested pair below becomes one v_max3).

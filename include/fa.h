@@ -43,7 +43,7 @@ enum {
   FA_ERR_SHAPE = -2,       /* a negative size, or sizes whose products overflow            */
   FA_ERR_UNSUPPORTED = -3, /* head dimension or dtype not built                            */
   FA_ERR_ALIGN = -4,       /* Q, K, V, O or a stride not 16-byte aligned; LSE/kv_len 4-byte */
-  FA_ERR_ARG = -5,         /* scale not finite and > 0, causal not 0/1, bad strides, O aliases */
+  FA_ERR_ARG = -5,         /* scale not finite, causal not 0/1, bad strides, O aliases */
   FA_ERR_HIP = -6          /* the kernel launch was rejected by the HIP runtime            */
 };
 
@@ -58,7 +58,8 @@ enum {
  *           fully masked row.
  * B, H, N, D : sizes. D must be 32, 64, 96 or 128 (or 256 for bf16/f16). If any of B, H,
  *           N is 0 the call does nothing and returns FA_OK (pointers are then not inspected).
- * scale   : softmax scale applied to Q.K^T; finite and > 0 (1/sqrt(D) is usual).
+ * scale   : softmax scale applied to Q.K^T; any finite value, of either sign or zero
+ *           (1/sqrt(D) is usual).
  * causal  : 1 for the causal mask, 0 for none.
  * kv_len  : device pointer to int32[B], valid key count per batch, or NULL for
  *           N everywhere. Values outside [0, N] are clamped to it by the kernel.

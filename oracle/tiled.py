@@ -3,32 +3,28 @@
 TEST INFRASTRUCTURE (see the package docstring): never imported by the
 product path.
 
-This is the recurrence the GPU kernel runs, written as the pages give it and
-kept in float64 so that it must agree with the naive definition to rounding
-order ("vectorized-flash-attention-kernel", Core algorithm; Key design
-decision 1, online softmax; decision 3, causal masking with whole-block skip).
-For each query block every row starts with m = -inf, l = 0, O = 0; for each
-key/value block:
+What this model is: the recurrence the GPU kernel runs, kept in float64, so that
+it must reach the naive definition up to the order of rounding. The method it
+follows is the one of "vectorized-flash-attention-kernel" (Core algorithm; Key
+design decisions 1, 3 and 4) and "js-flash-attention-tiled-online-softmax-
+exactness" (Root causes addressed 1 and 2).
 
-  1. S = scale * Q_block K_block^T;
-  2. masked scores (key after query under the causal mask, or key at or past
-     kv_len) become -inf;
-  3. m_new = max(m_old, max_j S_ij); correction = exp(m_old - m_new);
-     l = correction * l + sum_j exp(S_ij - m_new);
-     O = correction * O + sum_j exp(S_ij - m_new) V_j;
-     a row whose m_new is still -inf has seen no valid key and is left as it
-     is ("js-flash-attention-tiled-online-softmax-exactness", Root causes
-     addressed 2: exp(-inf - -inf) would be NaN);
-
-then O /= l, with exact zeros where l == 0 (Root causes addressed 2 tests l
-for zero, so a NaN that escaped the guard stays visible), and the per-row
-statistics are returned in compressed form as LSE = m + ln l (Key design
-decision 4 keeps the row max and row sum for the backward pass).
+In short: every query row carries a small state while the key blocks go by, its
+largest scaled logit so far, the sum of its exponentials taken relative to that
+largest value, and the matching weighted sum of value rows. A new key block
+contributes its own exponentials; when it raises the row's largest logit, the
+state held so far is first brought to the new reference by one exponential
+factor, which keeps every exponential at most 1 and so nothing overflows. A key
+after the query (causal mask) or at or past kv_len contributes nothing. A row
+that has not yet seen a valid key keeps the empty state, so the factor is never
+formed from two infinities. At the end the weighted sum is divided by the sum
+(exact zeros for an empty row, whose sum is exactly zero) and the two row
+statistics are returned folded into one number, LSE = largest logit + ln(sum).
 
 A key/value block is skipped when it lies wholly in the future of the query
-block: its first key index is greater than the block's last query index.
-Blocks wholly past every batch's kv_len are skipped too. All (b, h) are
-processed at once with array arithmetic; the loops are the pages' block loops.
+block (its first key index exceeds the block's last query index), and blocks
+wholly past every batch's kv_len are skipped too. All (b, h) are processed at
+once with array arithmetic; the two loops are the block loops.
 """
 
 import numpy as np

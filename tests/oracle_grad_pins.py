@@ -85,10 +85,11 @@ def pin_grad_torch_autograd(grad):
     q, k, v, do = _inputs(42, 2, 3, 9, 5, Dv=4)
     for causal in (False, True):
         for kv in (None, np.array([6, 0])):
-            want = torch_autograd(q, k, v, do, 0.45, causal, kv)
-            got = grad(q, k, v, do, 0.45, causal=causal, kv_len=kv)
-            for name, a, b in zip(("dQ", "dK", "dV"), got, want):
-                _close(a, b, 1e-11, 1e-12, f"autograd {name} causal={causal} kv={kv}")
+            for scale in (0.45, -0.45, 0.0):   # the scale carries no sign restriction
+                want = torch_autograd(q, k, v, do, scale, causal, kv)
+                got = grad(q, k, v, do, scale, causal=causal, kv_len=kv)
+                for name, a, b in zip(("dQ", "dK", "dV"), got, want):
+                    _close(a, b, 1e-11, 1e-12, f"autograd {name} causal={causal} kv={kv} scale={scale}")
 
 
 def pin_grad_invariants(grad):

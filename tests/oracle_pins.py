@@ -67,7 +67,7 @@ def pin_brute_force_exhaustive(attn):
             q = rng.integers(-8, 9, size=(1, 1, N, D)) / 4.0
             k = rng.integers(-8, 9, size=(1, 1, N, D)) / 4.0
             v = rng.integers(-8, 9, size=(1, 1, N, D + 1)) / 4.0
-            for scale in (1.0, 0.3):
+            for scale in (1.0, 0.3, -0.6):
                 for causal in (False, True):
                     for L in range(N + 1):
                         kv = np.array([L])
@@ -255,9 +255,34 @@ def pin_convex(attn):
             assert ((o[b, :, i] >= lo) & (o[b, :, i] <= hi)).all(), f"not convex b={b} i={i}"
 
 
+def pin_scale_sign(attn):
+    """A negative scale is the positive one applied to -Q (exactly, since negation is exact),
+    and matches 50-digit brute force; a zero scale weighs every valid key the same: O is the
+    mean of V over the valid prefix and LSE = ln(count), whatever Q and K hold."""
+    rng = np.random.default_rng(16)
+    q = rng.standard_normal((2, 2, 6, 3))
+    k = rng.standard_normal((2, 2, 6, 3))
+    v = rng.standard_normal((2, 2, 6, 4))
+    kv = np.array([6, 4])
+    for causal in (False, True):
+        neg = attn(q, k, v, -0.7, causal=causal, kv_len=kv)
+        flip = attn(-q, k, v, 0.7, causal=causal, kv_len=kv)
+        _close(neg[0], flip[0], 0.0, 0.0, f"negative scale = negated Q causal={causal} O")
+        _close(neg[1], flip[1], 0.0, 0.0, f"negative scale = negated Q causal={causal} LSE")
+        want = brute_force(q, k, v, -0.7, causal, kv)
+        _close(neg[0], want[0], 1e-13, 1e-14, f"negative scale brute causal={causal} O")
+        _close(neg[1], want[1], 1e-13, 1e-14, f"negative scale brute causal={causal} LSE")
+        o, lse = attn(q, k, v, 0.0, causal=causal, kv_len=kv)
+        for b in range(2):
+            for i in range(6):
+                cnt = min(int(kv[b]), i + 1) if causal else int(kv[b])
+                _close(o[b, :, i], v[b, :, :cnt].mean(axis=1), 1e-14, 1e-15, f"zero scale mean b={b} i={i}")
+                _close(lse[b, :, i], np.full(2, np.log(cnt)), 1e-14, 1e-15, f"zero scale LSE b={b} i={i}")
+
+
 ALL_PINS = [pin_brute_force_exhaustive, pin_brute_force_batched, pin_golden, pin_single_token,
             pin_zero_inputs, pin_identical_keys, pin_large_logits, pin_shift, pin_masks,
-            pin_permutation, pin_convex]
+            pin_permutation, pin_convex, pin_scale_sign]
 
 
 def pin_query_padding(attn):

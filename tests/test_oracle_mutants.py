@@ -3,10 +3,10 @@
 The mutants are made on the CPU from the oracle's own source text (a single
 substring replaced), so they are plausible slips in the code as written: a
 dropped term, a wrong sign or bound, a swapped operand. The tiled-model
-mutants follow the spirit of the "five one-line bugs in an online-softmax
-kernel" exercise (Paper: FlashAttention, Exercises): no rescale of l, no
-rescale of the accumulator, an off-by-one causal mask, no -inf guard,
-normalising inside the loop, and more.
+mutants include the slips that the exercise on breaking an online-softmax
+kernel on purpose asks about ("Paper: FlashAttention", Exercises): the sum or
+the accumulator left unrescaled, the causal mask off by one, the guard for an
+empty row dropped, the division by the sum done inside the loop, and more.
 """
 
 import inspect

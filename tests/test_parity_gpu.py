@@ -2,13 +2,16 @@
 
 Tolerances (fixed by the target, written here): float32 inputs, max |error| <= 1e-5;
 bf16/f16 inputs, |gpu - ref| <= 2e-2 + 1e-2*|ref| elementwise. The same bound
-applies to LSE, and -inf (fully masked rows) must match exactly; for float32 the LSE
-bound also allows two float32 spacings at the LSE's own magnitude (2^-22 * |LSE|),
-since LSE is stored in float32. Inputs come from the seeded generator; the oracle
-sees them upcast exactly to float64.
+applies to LSE, and -inf (fully masked rows) must match exactly. Only the tests whose
+logits are deliberately large (scaled logits near 100 and beyond) let the float32 LSE
+bound also allow two float32 spacings at the LSE's own magnitude (2^-22 * |LSE|): a
+float32 number of magnitude 100 is resolved only to 7.6e-6, so the stored LSE cannot be
+closer than that to the float64 value; each such test prints its measured error. Inputs
+come from the seeded generator; the oracle sees them upcast exactly to float64.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -47,7 +50,10 @@ def run_gpu(x, kv_len=None, causal=None, prefill_nan=True):
     return o, lse
 
 
-def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, lse_f32_spacing=False):
+    """Element by element against the oracle. Returns (max |O err|, max |LSE err|, max O
+    err/bound, max LSE err/bound). `lse_f32_spacing` adds 2^-22 * |LSE| to the float32 LSE
+    bound (large-logit tests only)."""
     atol, rtol = tol(dtype)
     o = o_gpu.detach().float().cpu().double().numpy()
     l = lse_gpu.detach().cpu().double().numpy()
@@ -61,9 +67,13 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
     assert (eo <= bo).all(), f"{what}: O max err {eo.max():.3e} (worst excess {(eo - bo).max():.3e})"
     fin = ~inf_ref
     el = np.abs(l[fin] - lse_ref[fin])
-    bl = atol + max(rtol, LSE_F32_RTOL if dtype == "f32" else 0.0) * np.abs(lse_ref[fin])
+    lrt = max(rtol, LSE_F32_RTOL) if (dtype == "f32" and lse_f32_spacing) else rtol
+    bl = atol + lrt * np.abs(lse_ref[fin])
     assert (el <= bl).all(), f"{what}: LSE max err {el.max() if el.size else 0:.3e}"
-    return float(eo.max(initial=0.0)), float(el.max(initial=0.0))
+    if lse_f32_spacing and dtype == "f32" and el.size:
+        say(f"  {what}: float32 LSE max err {el.max():.3e} at |LSE| up to {np.abs(lse_ref[fin]).max():.1f}")
+    return (float(eo.max(initial=0.0)), float(el.max(initial=0.0)), float((eo / bo).max(initial=0.0)),
+            float((el / bl).max(initial=0.0)))
 
 
 SWEEP_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
@@ -164,7 +174,7 @@ def test_large_negative_logits(dtype, causal):
     o, lse = run_gpu(x)
     ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
     assert rl.max() < -80
-    compare(o, lse, ro, rl, dtype, "large negative logits")
+    compare(o, lse, ro, rl, dtype, "large negative logits", lse_f32_spacing=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
@@ -183,14 +193,14 @@ def test_rising_and_jumping_logits(dtype, D, causal):
     x.k[..., -1] = 2.0 * torch.arange(N, dtype=torch.float32).to(x.k.dtype)
     o, lse = run_gpu(x)
     ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
-    compare(o, lse, ro, rl, dtype, "rising logits")
+    compare(o, lse, ro, rl, dtype, "rising logits", lse_f32_spacing=True)
     x = generate(1, 2, N, D, dtype, causal=causal, seed=88)
     x.q[..., -1] = 4.0
     x.k[..., -1] = 0.0
     x.k[:, :, 100, -1] = 60.0
     o, lse = run_gpu(x)
     ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
-    compare(o, lse, ro, rl, dtype, "jumping logit")
+    compare(o, lse, ro, rl, dtype, "jumping logit", lse_f32_spacing=True)
 
 
 def test_deterministic():
@@ -209,27 +219,15 @@ def test_empty_batch_is_noop():
     assert o.shape == q.shape and lse.shape == (0, 2, 16)
 
 
-def _sample_heads_rows(w, x, rng):
-    heads = {(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)}
-    if x.kv_len is not None:
-        heads.add((int(x.meta["zero_batch"]), 0))
-        nz = [b for b in range(w.B) if x.kv_len[b] > 0]
-        if nz:
-            heads.add((min(nz, key=lambda b: x.kv_len[b]), w.H - 1))
-    rows = {0, 1, 2, 31, 32, 127, 128, w.N // 2, w.N - 2, w.N - 1}
-    if x.kv_len is not None:
-        for L in x.kv_len:
-            for r in (int(L) - 1, int(L)):
-                if 0 <= r < w.N:
-                    rows.add(r)
-    rows |= set(rng.integers(0, w.N, size=24).tolist())
-    return sorted(heads), np.array(sorted(rows))
+def oracle_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_full_size_workload(name):
-    """Each named workload at full size, launched as the benchmark launches it: sampled
-    rows against the oracle, plus properties that hold at any size."""
+    """Each named workload at full size, launched as the benchmark launches it: every element
+    of O and LSE against the float64 oracle over the whole workload, plus properties that hold
+    at any size."""
     w = WORKLOADS[name]
     say(f"full-size workload {name}: generating inputs")
     x = generate_workload(w)
@@ -241,21 +239,19 @@ def test_full_size_workload(name):
         zb = int(x.meta["zero_batch"])
         assert (o[zb] == 0).all().item(), "fully masked batch must be exactly zero"
         assert (torch.isinf(lse[zb]) & (lse[zb] < 0)).all().item(), "fully masked batch must have LSE = -inf"
-    rng = np.random.default_rng(9)
-    heads, rows = _sample_heads_rows(w, x, rng)
-    ocpu = o.float().cpu()
-    lcpu = lse.cpu()
-    for b, h in heads:
-        say(f"full-size workload {name}: oracle rows of b={b} h={h}")
-        kv = None if x.kv_len is None else x.kv_len[b:b + 1]
-        ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
-                                  to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=w.causal, kv_len=kv, rows=rows)
-        compare(ocpu[b:b + 1, h:h + 1, rows], lcpu[b:b + 1, h:h + 1, rows], ro, rl, w.dtype, f"{name} b={b} h={h}")
     if w.causal:
         # Causal row 0 attends only to key 0 (in every batch that has a key at all).
         atol, _ = tol(w.dtype)
         live = [b for b in range(w.B) if x.kv_len is None or x.kv_len[b] > 0]
-        assert torch.allclose(ocpu[live, :, 0], x.v[live, :, 0].float(), atol=atol, rtol=0)
+        assert torch.allclose(o.float().cpu()[live, :, 0], x.v[live, :, 0].float(), atol=atol, rtol=0)
+    nw = oracle_workers()
+    say(f"full-size workload {name}: float64 oracle over all {w.B * w.H} heads x {w.N} rows ({nw} threads)")
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=w.causal, kv_len=x.kv_len,
+                              workers=nw)
+    eo, el, ratio_o, ratio_l = compare(o, lse, ro, rl, w.dtype, name)
+    del ro, rl
+    say(f"full-size workload {name}: all {o.numel()} elements of O and {lse.numel()} of LSE within bounds; "
+        f"max |O err| {eo:.3e} (err/bound {ratio_o:.3f}), max |LSE err| {el:.3e} (err/bound {ratio_l:.3f})")
     say(f"full-size workload {name}: determinism")
     o2, l2 = run_gpu(x)
     assert torch.equal(o, o2) and torch.equal(lse, l2)
@@ -358,3 +354,38 @@ def test_shared_kv_head(dtype):
     ro, rl = oracle.attention(to_f64(x.q), to_f64(k1.expand(B, H, N, D)), to_f64(v1.expand(B, H, N, D)),
                               x.scale, causal=True, kv_len=kv)
     compare(o, lse, ro, rl, dtype, "shared K/V head")
+
+
+# ---------------------------------------------------------------- scale of either sign
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 32), ("bf16", 64), ("bf16", 96),
+                                     ("bf16", 128), ("bf16", 256), ("f16", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_of_either_sign(dtype, D, causal):
+    """The softmax scale may be negative or zero ("vectorized-flash-attention-kernel",
+    Constructor options: softmaxScale carries no sign restriction). A negative scale makes the
+    row maximum that of s*scale, not scale*max(s); a zero scale weighs every valid key the
+    same. Padding keys hold NaN. The plain forward and the split forward (3 parts)."""
+    N = 200
+    kv = np.array([0, 1, 64, 131, 200], dtype=np.int32)
+    x = generate(5, 2, N, D, dtype, causal=causal, seed=3300 + D)
+    k0, v0 = x.k.clone(), x.v.clone()
+    for b, L in enumerate(kv):
+        x.k[b, :, L:] = float("nan")
+        x.v[b, :, L:] = float("nan")
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    kl = torch.as_tensor(kv)
+    for sc in (-x.scale, -3.0 * x.scale, 0.0):
+        say(f"scale {sc:+.4f} dtype={dtype} D={D} causal={causal}")
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(k0), to_f64(v0), sc, causal=causal, kv_len=kv)
+        for splits in (1, 3):
+            o, lse = fa.forward(q, k, v, causal=causal, scale=sc, kv_len=kl, n_splits=splits,
+                                out=torch.full_like(q, float("nan")),
+                                lse=torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev))
+            torch.cuda.synchronize()
+            compare(o, lse, ro, rl, dtype, f"scale {sc:+.4f} splits {splits}")
+        if sc == 0.0:
+            counts = np.minimum(kv[:, None], np.arange(1, N + 1)[None, :]) if causal else np.repeat(kv[:, None], N, 1)
+            want = np.where(counts > 0, np.log(np.maximum(counts, 1)), -np.inf)
+            got = lse.cpu().double().numpy()
+            assert np.allclose(got, np.broadcast_to(want[:, None, :], got.shape), atol=tol(dtype)[0], rtol=0)

@@ -16,7 +16,7 @@ import oracle
 import exact_tiled_attention_23_amd as fa
 from exact_tiled_attention_23_amd.workloads import generate, generate_grad_output, to_f64
 
-from test_backward_gpu import DTYPE_NAME, compare_grad, rounding_bound
+from grad_bounds import DTYPE_NAME, compare_grad, rounding_bound
 from test_parity_gpu import compare, say
 
 pytestmark = pytest.mark.gpu
