@@ -63,6 +63,11 @@ __device__ __forceinline__ float pair_max(float x) {
   return m;
 }
 
+// IEEE maximum of three values (NaN-propagating): one v_maximum3_f32.
+__device__ __forceinline__ float fmax3_ieee(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -360,7 +365,9 @@ void fwd16_kernel(FwdParams p) {
       }
       float mx;
       {
-        // 16*NSUB values in three-input maxima (each nested pair below becomes one v_max3).
+        // 16*NSUB values in three-input maxima (each nested pair below becomes one
+        // v_maximum3_f32). The IEEE maximum propagates NaN instead of quieting its operands, so
+        // the masked exponents (a select) need no canonicalising max of their own.
         constexpr int NV = 16 * NSUB;
         float m[NV];
 #pragma unroll
@@ -371,8 +378,8 @@ void fwd16_kernel(FwdParams p) {
           if (cnt > 1) {
             int o = 0, i = 0;
 #pragma unroll
-            for (; i + 2 < cnt; i += 3) m[o++] = fmaxf(fmaxf(m[i], m[i + 1]), m[i + 2]);
-            if (cnt - i == 2) m[o++] = fmaxf(m[i], m[i + 1]);
+            for (; i + 2 < cnt; i += 3) m[o++] = fmax3_ieee(m[i], m[i + 1], m[i + 2]);
+            if (cnt - i == 2) m[o++] = __builtin_elementwise_maximum(m[i], m[i + 1]);
             else if (cnt - i == 1) m[o++] = m[i];
             cnt = o;
           }
