@@ -15,8 +15,11 @@ from .build import LIB
 
 FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_ARG, FA_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+FA_ERR_TOO_LARGE = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
 EXPORTED = ("fa_fwd", "fa_fwd_strided", "fa_fwd_split_workspace_bytes", "fa_fwd_split", "fa_fwd_split_count",
-            "fa_merge_states", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_strerror", "fa_abi_version")
+            "fa_merge_states", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_strided", "fa_bwd_noalloc", "fa_strerror",
+            "fa_abi_version")
 MAX_SPLITS = 256
 
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
@@ -65,6 +68,9 @@ def load_library():
         lib.fa_bwd_strided.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
             ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_bwd_noalloc.restype = ctypes.c_int
+        lib.fa_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_abi_version.restype = ctypes.c_int
@@ -138,6 +144,12 @@ def fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, strides, scale, 
     arr = _int64_array(strides, 24, "strides")
     return load_library().fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, arr, scale, causal, q_len,
                                          kv_len, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype, stream):
+    """Raw C call of the backward whose workspace is the library's static scratch array."""
+    return load_library().fa_bwd_noalloc(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype,
+                                         stream)
 
 
 def fa_strerror(code):

@@ -1,11 +1,13 @@
 // C ABI of the attention forward, key-split forward, partial-state merge and backward
 // (declared in include/fa.h): argument checks and kernel dispatch. Every check runs before
-// any kernel launch; the library keeps no state and allocates nothing.
+// any kernel launch; the library allocates nothing. Its only state is the per-device address
+// of the static scratch array that fa_bwd_noalloc uses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_fwd_kernel.h"
@@ -15,7 +17,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kWaves = 4;      // waves per workgroup: 4 x 32 = 128 query rows per tile
 constexpr int kBlockKV = 64;   // keys per K/V tile
 // bf16/f16 kernel shape per head dimension: keys per K/V tile, waves per workgroup (32
@@ -255,6 +257,7 @@ extern "C" const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "misaligned pointer or stride (Q, K, V, O and their strides need 16 bytes; LSE, q_len and kv_len 4 bytes)";
     case FA_ERR_ARG: return "invalid argument (scale finite, causal 0 or 1, strides >= 0, outputs not aliasing inputs nor themselves, part count in range, workspace large enough)";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_TOO_LARGE: return "the problem needs more than the static scratch of fa_bwd_noalloc (FA_NOALLOC_SCRATCH_BYTES); call fa_bwd with a workspace";
     default: return "unknown error code";
   }
 }
@@ -511,6 +514,61 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
                       void* stream) {
   return fa_bwd_strided(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, nullptr, scale, causal, nullptr, kv_len, dtype,
                         workspace, workspace_bytes, stream);
+}
+
+// ---- fa_bwd_noalloc: fa_bwd with its workspace in a file-scope device array, for callers that
+// cannot allocate. In host code `scratch` names a host-side stand-in, never the device memory:
+// host code uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_address[kMaxScratchDevices];  // device address of `scratch` per device, once looked up
+
+// The device address of `scratch` on the device of `stream` (the current device for the null
+// stream), looked up once per device with that device current.
+int scratch_on(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+  int dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_address[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || !p) return FA_ERR_HIP;
+    scratch_address[dev] = p;
+  }
+  *out = scratch_address[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                              const void* dO, void* dQ, void* dK, void* dV, int64_t B, int64_t H, int64_t N,
+                              int64_t D, float scale, int causal, const int32_t* kv_len, int dtype, void* stream) {
+  bool empty;
+  int rc = bwd_precheck(B, H, N, D, scale, causal, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  const int64_t need = fa_bwd_workspace_bytes(B, H, N, D);
+  if (need < 0) return FA_ERR_SHAPE;
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  // The caller's pointers are checked before the first HIP call; fa_bwd checks everything again.
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL;
+  for (const void* ptr : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV})
+    if (misaligned(ptr, 16)) return FA_ERR_ALIGN;
+  if (misaligned(LSE, 4) || (kv_len && misaligned(kv_len, 4))) return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  rc = scratch_on(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (rc != FA_OK) return rc;
+  return fa_bwd(Q, K, V, O, LSE, dO, dQ, dK, dV, B, H, N, D, scale, causal, kv_len, dtype, ws,
+                FA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int fa_fwd_strided(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,

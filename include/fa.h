@@ -44,7 +44,8 @@ enum {
   FA_ERR_UNSUPPORTED = -3, /* head dimension or dtype not built                            */
   FA_ERR_ALIGN = -4,       /* Q, K, V, O or a stride not 16-byte aligned; LSE/kv_len 4-byte */
   FA_ERR_ARG = -5,         /* scale not finite, causal not 0/1, bad strides, O aliases */
-  FA_ERR_HIP = -6          /* the kernel launch was rejected by the HIP runtime            */
+  FA_ERR_HIP = -6,         /* the kernel launch was rejected by the HIP runtime            */
+  FA_ERR_TOO_LARGE = -7    /* fa_bwd_noalloc: the problem needs more than its static scratch */
 };
 
 /*
@@ -245,6 +246,30 @@ int fa_bwd_strided(const void* Q, const void* K, const void* V, const void* O, c
                    int64_t B, int64_t H, int64_t N, int64_t D, const int64_t* strides,
                    float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
                    int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_noalloc - fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid hipMalloc): the same
+ * arguments, arithmetic, outputs and errors as fa_bwd, without the workspace arguments. Its
+ * workspace is a static device array of FA_NOALLOC_SCRATCH_BYTES bytes inside this library,
+ * one copy per GPU, held until the process ends. The call allocates nothing and frees nothing.
+ *
+ * Limit: fa_bwd_workspace_bytes(B, H, N, D) <= FA_NOALLOC_SCRATCH_BYTES, i.e. B*H*ceil(N/64)
+ * <= 65536 blocks of 64 rows (e.g. B*H = 64 heads of N = 65536); a larger problem returns
+ * FA_ERR_TOO_LARGE before any HIP call.
+ * Sharing: every call on one GPU uses that GPU's array, which keeps the last call's contents
+ * (each call writes every entry it reads before reading it). Calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race on the array:
+ * order them on one stream. The first call on a GPU looks up the array's device address
+ * (hipGetSymbolAddress with that GPU current) and keeps it for later calls.
+ * stream : as for fa_bwd; the array of the stream's device is used (the current device for
+ *          the null stream).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32LL << 20)
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                   const void* dO, void* dQ, void* dK, void* dV,
+                   int64_t B, int64_t H, int64_t N, int64_t D, float scale, int causal,
+                   const int32_t* kv_len, int dtype, void* stream);
 
 /* Static, human-readable text for a return code of fa_fwd. Never NULL. */
 const char* fa_strerror(int code);

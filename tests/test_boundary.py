@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strerror():
-    assert fa.fa_abi_version() == 6
+    assert fa.fa_abi_version() == 7
     codes = [0, -1, -2, -3, -4, -5, -6]
     texts = [fa.fa_strerror(c) for c in codes]
     assert len(set(texts)) == len(codes) and all(texts)
@@ -395,3 +395,31 @@ def test_bwd_strided_layout_rules():
     assert call_bwd_strided(s, dK=BG["dQ"]) == binding.FA_ERR_ARG   # two outputs at one address
     assert call_bwd_strided(s, dV=BG["K"]) == binding.FA_ERR_ARG    # output on an input
     assert call_bwd_strided(None, N=0, Q=0) == binding.FA_OK
+
+
+def call_bwd_noalloc(**kw):
+    a = dict(BG)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["dO"], a["dQ"], a["dK"], a["dV"], a["B"],
+                             a["H"], a["N"], a["D"], a["scale"], a["causal"], a["kv_len"], a["dtype"], a["stream"])
+
+
+def test_bwd_noalloc_validation_before_any_hip_call():
+    """The allocation-free backward checks its arguments, and that its workspace fits the static
+    scratch array, before its first HIP call (so these run without a GPU)."""
+    assert binding.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert call_bwd_noalloc(B=-1) == binding.FA_ERR_SHAPE
+    assert call_bwd_noalloc(dtype=fa.FA_F32) == binding.FA_ERR_UNSUPPORTED
+    assert call_bwd_noalloc(D=256) == binding.FA_ERR_UNSUPPORTED
+    assert call_bwd_noalloc(scale=float("nan")) == binding.FA_ERR_ARG
+    assert call_bwd_noalloc(causal=2) == binding.FA_ERR_ARG
+    assert call_bwd_noalloc(B=0) == binding.FA_OK
+    for f in ("Q", "K", "V", "O", "LSE", "dO", "dQ", "dK", "dV"):
+        assert call_bwd_noalloc(**{f: 0}) == binding.FA_ERR_NULL, f
+    for f in ("Q", "K", "V", "O", "dO", "dQ", "dK", "dV"):
+        assert call_bwd_noalloc(**{f: BG[f] + 8}) == binding.FA_ERR_ALIGN, f
+    # 65536 blocks of 64 rows fit (64 heads of N = 65536); one row more does not.
+    assert fa.fa_bwd_workspace_bytes(1, 64, 65536, 128) == binding.NOALLOC_SCRATCH_BYTES
+    assert call_bwd_noalloc(B=1, H=64, N=65537, D=128) == binding.FA_ERR_TOO_LARGE
+    assert call_bwd_noalloc(B=64, H=64, N=65536, D=64) == binding.FA_ERR_TOO_LARGE
+    assert "static scratch" in fa.fa_strerror(binding.FA_ERR_TOO_LARGE)
