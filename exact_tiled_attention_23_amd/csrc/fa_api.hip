@@ -12,6 +12,7 @@
 #include "fa.h"
 #include "fa_fwd_kernel.h"
 #include "fa_fwd_mfma16.h"
+#include "fa_fwd_wsplit.h"
 #include "fa_merge.h"
 #include "fa_bwd.h"
 
@@ -103,10 +104,56 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Problems of at most this many 128-row query tiles fill a small part of the GPU; the float32
+// forward then runs 32-row query blocks whose key tiles are split over the waves of each
+// workgroup (fwd_wsplit_kernel), which shortens the longest chain of key tiles a wave walks.
+constexpr int64_t kWaveSplitMaxTiles = 64;
+template <int D> struct WSplitWaves { static constexpr int NW = D <= 64 ? 8 : 4; };
+
+template <typename T, int D>
+int launch_wsplit(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
+                  int64_t N, const Strides& st, float scale, int causal, const int32_t* q_len,
+                  const int32_t* kv_len, hipStream_t stream) {
+  constexpr int NW = WSplitWaves<D>::NW;
+  fa::FwdParams p;
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = LSE;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.q_sb = st.q[0]; p.q_sh = st.q[1]; p.q_sn = st.q[2];
+  p.k_sb = st.k[0]; p.k_sh = st.k[1]; p.k_sn = st.k[2];
+  p.v_sb = st.v[0]; p.v_sh = st.v[1]; p.v_sn = st.v[2];
+  p.o_sb = st.o[0]; p.o_sh = st.o[1]; p.o_sn = st.o[2];
+  p.H = H;
+  p.N = N;
+  p.scale_log2 = scale * fa::kLog2e;
+  p.causal = causal;
+  const int64_t n_blocks = (N + 31) / 32;
+  const int64_t units = B * H * n_blocks;
+  if (units > INT32_MAX) return FA_ERR_SHAPE;
+  p.n_qtiles = (int)n_blocks;
+  p.n_units = units;
+  p.n_splits = 1;
+  p.BH = B * H;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fwd_wsplit_kernel<T, D, NW>), dim3((unsigned)units),
+                                 dim3(64 * NW), args, 0, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
            const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
            hipStream_t stream, const Split& sp = Split()) {
+  if constexpr (sizeof(T) == 4) {
+    if (sp.n == 1 && B * H * ((N + 127) / 128) <= kWaveSplitMaxTiles)
+      return launch_wsplit<T, D>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream);
+  }
   if constexpr (sizeof(T) == 2 && (D == 96 || D == 128)) {
     static_assert(Shape16<D>::NW == 8, "the narrow shape halves an 8-wave workgroup");
     if (sp.n == 1 && causal && B * H * ((N + 255) / 256) < kNarrowBelowUnits)

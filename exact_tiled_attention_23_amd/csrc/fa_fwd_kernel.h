@@ -353,7 +353,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
       // ---- masks: only where the tile crosses the kv_len edge or this wave's diagonal. A dead
       // key's scaled logit is -inf and its probability 0, for a scale of either sign (or zero).
-      const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq;
+      // (Rows at or past N are never stored: only rows of query padding below N need the mask.)
+      const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > qw) || (nq < N && qw + 32 > nq);
       auto dead = [&](int u, int i) __attribute__((always_inline)) {
         const int64_t key = j0 + 32 * u + acc_key<KPER>(i, g);
         return key >= kvl || (p.causal && key > qrow) || qrow >= nq;

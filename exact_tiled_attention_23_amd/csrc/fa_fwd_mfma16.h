@@ -189,6 +189,8 @@ void fwd16_kernel(FwdParams p) {
   }
   if (q0 >= nq) kv_hi = 0;
   if (qw >= nq) wave_hi = 0;
+  // This wave holds rows before q_len and rows of query padding that are stored (O = 0).
+  const bool qpad_wave = nq < n && qw + 32 > nq;
   // Both bounds are wave-uniform; saying so keeps the per-tile tests on them scalar branches
   // (the compiler otherwise forms the three-way minimum in a vector register).
   kv_hi = __builtin_amdgcn_readfirstlane(kv_hi);
@@ -349,11 +351,12 @@ void fwd16_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) x[u][i] = __builtin_fmaf(s[u][i], c, nmuse);
 
       // ---- masks (edge tiles, and every tile of the wave that holds the last query rows
-      // before padding): key j0 + 32u + acc_key(i, g) is dead when it is at or past kv_len,
-      // or (causal) after this lane's query, or this lane's query is padding. The exponent is
-      // set to -inf after the scaling, so the mask holds for a scale of either sign (or zero)
-      // and whatever a padding key's score holds.
-      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qw + 32 > nq) {
+      // before query padding): key j0 + 32u + acc_key(i, g) is dead when it is at or past
+      // kv_len, or (causal) after this lane's query, or this lane's query is padding. The
+      // exponent is set to -inf after the scaling, so the mask holds for a scale of either sign
+      // (or zero) and whatever a padding key's score holds. Rows at or past N are never stored,
+      // so the wave that holds the tensor's last rows needs no mask of its own.
+      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qpad_wave) {
         int lim = qrow < nq ? kvl - j0 : 0;
         if (p.causal) lim = min(lim, qrow - j0 + 1);
         lim -= 8 * g;

@@ -389,3 +389,25 @@ def test_scale_of_either_sign(dtype, D, causal):
             want = np.where(counts > 0, np.log(np.maximum(counts, 1)), -np.inf)
             got = lse.cpu().double().numpy()
             assert np.allclose(got, np.broadcast_to(want[:, None, :], got.shape), atol=tol(dtype)[0], rtol=0)
+
+
+# ---------------------------------------------------------------- float32: both forward paths
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_wave_split_and_regular_paths(D, causal):
+    """float32 problems of at most 64 query tiles of 128 rows run 32-row blocks whose key tiles
+    are split over the waves of a workgroup and merged through LDS; larger ones run the regular
+    kernel. Shapes on both sides of that line (64 and 65 tiles of 128 rows, ragged N, key
+    padding with NaN-filled padding keys), every element against the oracle."""
+    for B, H, N in ((2, 4, 1000), (5, 13, 129), (1, 1, 1), (1, 1, 33)):
+        tiles = B * H * ((N + 127) // 128)
+        say(f"f32 paths D={D} causal={causal} B={B} H={H} N={N} ({tiles} tiles of 128 rows)")
+        x = generate(B, H, N, D, "f32", causal=causal, seed=3400 + N + D)
+        kv = np.array([max(N - 17 * b, 0) for b in range(B)], dtype=np.int32)
+        k0, v0 = x.k.clone(), x.v.clone()
+        for b, L in enumerate(kv):
+            x.k[b, :, L:] = float("nan")
+            x.v[b, :, L:] = float("nan")
+        o, lse = run_gpu(x, kv_len=kv)
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(k0), to_f64(v0), x.scale, causal=causal, kv_len=kv)
+        compare(o, lse, ro, rl, "f32", f"B={B} H={H} N={N}")
