@@ -380,8 +380,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
     tile_step(t + 1, Int<1>{});
   }
 
-  // ---- dQ = scale * acc; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4.
-  if (qrow < n) {
+  // ---- dQ = scale * acc; register i of block dt holds d = 32dt + 8(i/4) + 4g + i%4. The row's
+  // 64-bit offset is formed here from its 32-bit index (an opaque copy keeps the compiler from
+  // forming it before the loop and holding two more registers through it).
+  int qrow_out = qrow;
+  asm volatile("" : "+v"(qrow_out));
+  if (qrow_out < n) {
+    T* drow = dQh + (int64_t)qrow_out * p.st_dq.n + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
         T o4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (T)(acc[dt][4 * a4 + e] * p.scale);
-        *reinterpret_cast<uint2*>(dQh + (int64_t)qrow * p.st_dq.n + 32 * dt + 8 * a4 + 4 * g) = *reinterpret_cast<const uint2*>(o4);
+        *reinterpret_cast<uint2*>(drow + 32 * dt + 8 * a4) = *reinterpret_cast<const uint2*>(o4);
       }
   }
 }
@@ -789,18 +794,17 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
     frag tto[2], ttq[2];
     ttq[0] = tr_frag<T, D>(qb, 32 * qh, 0, lane);
     tto[0] = tr_frag<T, D>(ob, 32 * qh, 0, lane);
-    // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key.
-    float mo[16], dl[16];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float4* pm = reinterpret_cast<const float4*>(sb + 32 * qh + 16 * h + 8 * g);
-      const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * qh + 16 * h + 8 * g);
+    // Register i of half g holds query qs + 16(i/8) + 8g + i%8 of this lane's key. The queries'
+    // exponent offsets and -Delta come from LDS 8 at a time (per 16-query half), as needed.
+    auto stats8 = [&](int hh, float* mo8, float* dl8) __attribute__((always_inline)) {
+      const float4* pm = reinterpret_cast<const float4*>(sb + 32 * qh + 16 * hh + 8 * g);
+      const float4* pd = reinterpret_cast<const float4*>(sb + kStatRows + 32 * qh + 16 * hh + 8 * g);
       const float4 m0 = pm[0], m1 = pm[1], d0 = pd[0], d1 = pd[1];
-      mo[8 * h + 0] = m0.x; mo[8 * h + 1] = m0.y; mo[8 * h + 2] = m0.z; mo[8 * h + 3] = m0.w;
-      mo[8 * h + 4] = m1.x; mo[8 * h + 5] = m1.y; mo[8 * h + 6] = m1.z; mo[8 * h + 7] = m1.w;
-      dl[8 * h + 0] = d0.x; dl[8 * h + 1] = d0.y; dl[8 * h + 2] = d0.z; dl[8 * h + 3] = d0.w;
-      dl[8 * h + 4] = d1.x; dl[8 * h + 5] = d1.y; dl[8 * h + 6] = d1.z; dl[8 * h + 7] = d1.w;
-    }
+      mo8[0] = m0.x; mo8[1] = m0.y; mo8[2] = m0.z; mo8[3] = m0.w;
+      mo8[4] = m1.x; mo8[5] = m1.y; mo8[6] = m1.z; mo8[7] = m1.w;
+      dl8[0] = d0.x; dl8[1] = d0.y; dl8[2] = d0.z; dl8[3] = d0.w;
+      dl8[4] = d1.x; dl8[5] = d1.y; dl8[6] = d1.z; dl8[7] = d1.w;
+    };
     const bool diag = p.causal && qs < kw + 31;
     frag pf[2], dsf[2];
     // Masks only where a key of the wave is padding or the tile meets the diagonal (a
@@ -812,18 +816,30 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
       // lim: always for a padding key, never off the diagonal.
       const int lim = key_dead ? INT_MAX : (diag ? key - qs - 8 * g : INT_MIN);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
-        x = (16 * (i / 8) + (i % 8) < lim) ? 0.f : x;
-        pf[i / 8][i % 8] = (T)x;
-        dsf[i / 8][i % 8] = (T)(x * (dp[i] + dl[i]));  // dl holds -Delta
+      for (int hh = 0; hh < 2; ++hh) {
+        float mo[8], dl[8];
+        stats8(hh, mo, dl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * hh + e;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[e]));
+          x = (16 * hh + e < lim) ? 0.f : x;
+          pf[hh][e] = (T)x;
+          dsf[hh][e] = (T)(x * (dp[i] + dl[e]));  // dl holds -Delta
+        }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[i]));
-        pf[i / 8][i % 8] = (T)x;
-        dsf[i / 8][i % 8] = (T)(x * (dp[i] + dl[i]));  // dl holds -Delta
+      for (int hh = 0; hh < 2; ++hh) {
+        float mo[8], dl[8];
+        stats8(hh, mo, dl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 8 * hh + e;
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -mo[e]));
+          pf[hh][e] = (T)x;
+          dsf[hh][e] = (T)(x * (dp[i] + dl[e]));  // dl holds -Delta
+        }
       }
     }
     // dV^T += dO^T . P and dK^T += Q^T . dS, reading pair j+1 while pair j's products run.

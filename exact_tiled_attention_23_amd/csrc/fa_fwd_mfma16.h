@@ -47,6 +47,12 @@ template <int V> struct Int { static constexpr int value = V; };
 
 // Reference maximum may lag the true row maximum by up to this much (base-2 units).
 constexpr float kRescaleSlack = 8.0f;
+constexpr float kSlackSum = 256.0f;      // 2^kRescaleSlack
+// A tile whose reference was not tested first must keep every probability at most this large
+// (through each lane's sum of them); beyond it the workgroup computes again with every tile tested.
+constexpr float kUntestedSumBound = 65536.0f;
+// Tiles at the start, and after each move of the reference, that test it first.
+constexpr int kCalmTiles = 2;
 
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
@@ -282,10 +288,24 @@ void fwd16_kernel(FwdParams p) {
   float lsum = 0.f;        // this lane half's share of the denominator
   const float c = p.scale_log2;
 
+  // Testing the reference. Edge tiles, the first tiles of a unit and the tiles right after a
+  // move of the reference take the row maximum of their exponents first (the decision below).
+  // Elsewhere the reference rarely moves, and the tile skips the maximum: its probabilities are
+  // formed against the current reference and each lane's sum of them is checked afterwards. A sum
+  // above 2^slack only makes the next tile test again (the probabilities are exact for any
+  // reference while nothing overflows); a sum above kUntestedSumBound (or infinite, or NaN) is an
+  // overflow, and the whole workgroup then computes its unit again with every tile tested.
+  // The last key tile of the unit is always tested, so every wave has reported an overflow
+  // (one LDS word, cleared before the first tile's barrier) before the barrier of that tile, and
+  // after the loop every wave reads the same word without another barrier.
+  int calm = 0;              // wave-uniform: tiles since the reference last moved
+  bool test_all = false;     // the second pass, after an overflow
+  __shared__ int overflow_flag;
+  if (threadIdx.x == 0) overflow_flag = 0;
+
   // Tile t lives in buffer (t - t_lo) & 1 and is copied one tile ahead. The loop below runs
   // two tiles per iteration, one per buffer, so the buffer is a compile-time constant in each
   // copy of the body and every LDS address is a per-lane register plus an immediate offset.
-  if (t_lo < t_hi) issue_tile(t_lo * BC, Int<0>{});
 
   auto tile_step = [&](const int t, auto buf_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
@@ -356,7 +376,8 @@ void fwd16_kernel(FwdParams p) {
       // exponent is set to -inf after the scaling, so the mask holds for a scale of either sign
       // (or zero) and whatever a padding key's score holds. Rows at or past N are never stored,
       // so the wave that holds the tensor's last rows needs no mask of its own.
-      if (j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qpad_wave) {
+      const bool edge = j0 + BC > kvl || (p.causal && j0 + BC - 1 > qw) || qpad_wave;
+      if (edge) {
         int lim = qrow < nq ? kvl - j0 : 0;
         if (p.causal) lim = min(lim, qrow - j0 + 1);
         lim -= 8 * g;
@@ -366,6 +387,8 @@ void fwd16_kernel(FwdParams p) {
           for (int i = 0; i < 16; ++i)
             if (32 * u + 16 * (i / 8) + (i % 8) >= lim) x[u][i] = -INFINITY;
       }
+      const bool tested = edge || calm < kCalmTiles || test_all || t + 1 == t_hi;
+      if (tested) {
       float mx;
       {
         // 16*NSUB values in three-input maxima (each nested pair below becomes one
@@ -391,7 +414,9 @@ void fwd16_kernel(FwdParams p) {
       }
       // Move the reference when some row's maximum rose more than the slack above it, or when
       // a row sees its first valid key (its reference is still -inf).
+      calm = calm + 1;
       if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
+        calm = 0;
         const float mnew = fmaxf(mref, mx - nmuse);
         if (mnew != mref) {
           const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
@@ -409,8 +434,10 @@ void fwd16_kernel(FwdParams p) {
           nmuse = -mnew;
         }
       }
+      }
       // ---- probabilities and O^T += V^T . P^T, one 32-key sub-tile at a time, so the
       // vector work on one sub-tile can run while the matrix core works on another.
+      float tsum = 0.f;  // this lane's sum of the tile's probabilities
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         frag va[2][NDT];
@@ -433,7 +460,9 @@ void fwd16_kernel(FwdParams p) {
           a0 += x[u][i];
           a1 += x[u][i + 1];
         }
-        lsum += a0 + a1;
+        const float part = a0 + a1;
+        lsum += part;
+        tsum += part;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           frag pf;
@@ -445,12 +474,31 @@ void fwd16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);  // the V^T transpose reads
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
       }
+      if (!tested) {
+        calm = __any(tsum > kSlackSum) ? 0 : calm + 1;
+        if (__any(!(tsum <= kUntestedSumBound)) && lane == 0) overflow_flag = 1;
+      }
     }
   };
-  for (int t = t_lo; t < t_hi; t += 2) {
-    tile_step(t, Int<0>{});
-    if (t + 1 >= t_hi) break;
-    tile_step(t + 1, Int<1>{});
+  auto tile_loop = [&]() __attribute__((always_inline)) {
+    if (t_lo < t_hi) issue_tile(t_lo * BC, Int<0>{});
+    for (int t = t_lo; t < t_hi; t += 2) {
+      tile_step(t, Int<0>{});
+      if (t + 1 >= t_hi) break;
+      tile_step(t + 1, Int<1>{});
+    }
+  };
+  tile_loop();
+  if (t_lo < t_hi && *static_cast<volatile int*>(&overflow_flag)) {
+    __syncthreads();  // every wave is done with the tiles, so the buffers can be refilled
+    test_all = true;
+    calm = 0;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+    mref = -INFINITY;
+    nmuse = 0.f;
+    lsum = 0.f;
+    tile_loop();
   }
 
   // ---- epilogue

@@ -411,3 +411,30 @@ def test_f32_wave_split_and_regular_paths(D, causal):
         o, lse = run_gpu(x, kv_len=kv)
         ro, rl = oracle.attention(to_f64(x.q), to_f64(k0), to_f64(v0), x.scale, causal=causal, kv_len=kv)
         compare(o, lse, ro, rl, "f32", f"B={B} H={H} N={N}")
+
+
+# ---------------------------------------------------------------- untested tiles: sum check and retry
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_jumps_after_quiet_tiles(dtype, D, causal):
+    """After a few quiet key tiles the 16-bit kernels form a tile's probabilities without first
+    taking its row maximum, and check each lane's sum of them instead. One key whose base-2 logit
+    stands about 12, 40 or 200 above the rest, placed well past the tiles that test the reference
+    first (key 300 of 1000, and a second one at key 700), exercises the three outcomes: a sum above
+    2^8 (the next tile tests again), a sum beyond the bound (the workgroup computes its unit
+    again, every tile tested), and an infinite sum. Each against the oracle."""
+    N = 1000
+    c = float(np.float32(1.0 / np.sqrt(D))) * 1.4426950408889634   # base-2 logit per unit of q.k
+    for jump in (12.0, 40.0, 200.0):
+        say(f"reference jump +{jump} dtype={dtype} D={D} causal={causal}")
+        x = generate(2, 2, N, D, dtype, causal=causal, seed=3500 + D + int(jump))
+        x.q[..., -1] = 1.0
+        x.k[..., -1] = 0.0
+        x.k[:, :, 300, -1] = jump / c
+        x.k[:, 1, 700, -1] = 1.5 * jump / c
+        o, lse = run_gpu(x)
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+        compare(o, lse, ro, rl, dtype, f"jump +{jump}")
+        o2, l2 = run_gpu(x)
+        assert torch.equal(o, o2) and torch.equal(lse, l2), "not deterministic"
