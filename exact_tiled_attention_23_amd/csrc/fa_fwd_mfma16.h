@@ -50,7 +50,9 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr float kSlackSum = 256.0f;      // 2^kRescaleSlack
 // A tile whose reference was not tested first must keep every probability at most this large
 // (through each lane's sum of them); beyond it the workgroup computes again with every tile tested.
-constexpr float kUntestedSumBound = 65536.0f;
+// Below float16's largest finite value, so no probability that passes rounds to infinity when it
+// is converted for the product with V.
+constexpr float kUntestedSumBound = 32768.0f;
 // Tiles at the start, and after each move of the reference, that test it first.
 constexpr int kCalmTiles = 2;
 

@@ -438,3 +438,27 @@ def test_reference_jumps_after_quiet_tiles(dtype, D, causal):
         compare(o, lse, ro, rl, dtype, f"jump +{jump}")
         o2, l2 = run_gpu(x)
         assert torch.equal(o, o2) and torch.equal(lse, l2), "not deterministic"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_untested_probability_near_float16_limit(dtype, D, causal):
+    """One key whose probability, taken against a reference fixed by earlier tiles, lands on an
+    untested tile at 2^14.9 (finite in float16, below the sum bound: kept) and at 2^15.9999
+    (about 65531, which rounds to infinity in float16: the sum bound must send the unit to the
+    all-tested pass). Every other key after the first two tiles has a negligible probability,
+    so that lane's sum is that one probability. Against the oracle."""
+    N = 512
+    for lg in (14.9, 15.9999):
+        say(f"untested probability 2^{lg} dtype={dtype} D={D} causal={causal}")
+        x = generate(1, 2, N, D, dtype, causal=causal, seed=3600 + D)
+        x.scale = float(np.float32(lg / 1.4426950408889634))  # base-2 logit of q.k = 1
+        x.q.zero_()
+        x.q[..., 0] = 1.0
+        x.k.zero_()                 # keys 0..127: logit 0, which fixes the reference at 0
+        x.k[:, :, 128:, 0] = -2.0   # then probabilities of about 2^-32
+        x.k[:, :, 300, 0] = 1.0     # one key at the chosen logit, in a later (untested) tile
+        o, lse = run_gpu(x)
+        ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
+        compare(o, lse, ro, rl, dtype, f"probability 2^{lg}")
