@@ -363,6 +363,28 @@ void fwd16_kernel(FwdParams p) {
         }
       }
 
+      // ---- V^T fragments (transpose reads). At D = 64..128 those of the whole tile are read
+      // here, so their latency passes under the vector work below; at D = 32 (128-key tiles)
+      // and D = 256 they would not fit in registers beside the rest, and each sub-tile reads
+      // its own just before its products.
+      constexpr bool kHoistV = D >= 64 && D <= 128;
+      frag vall[kHoistV ? NSUB : 1][2][NDT];
+      auto read_v = [&](int u, frag (&dst)[2][NDT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            const unsigned char* vp = vb + (32 * u + 16 * h) * ROWB + voff[dt];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
+            dst[h][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+      };
+      if constexpr (kHoistV) {
+#pragma unroll
+        for (int u = 0; u < NSUB; ++u) read_v(u, vall[u]);
+      }
+
       // ---- online softmax: the exponents x = s*c - mref of the whole tile (s*c while mref is
       // -inf), and one decision per tile on moving the reference, from the row maximum over
       // all of the tile's keys.
@@ -442,16 +464,8 @@ void fwd16_kernel(FwdParams p) {
       float tsum = 0.f;  // this lane's sum of the tile's probabilities
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        frag va[2][NDT];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const unsigned char* vp = vb + (32 * u + 16 * h) * ROWB + voff[dt];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 4 * ROWB));
-            va[h][dt] = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
+        if constexpr (!kHoistV) read_v(u, vall[0]);
+        frag (&va)[2][NDT] = vall[kHoistV ? u : 0];
         x[u][0] = __builtin_amdgcn_exp2f(x[u][0]);
         x[u][1] = __builtin_amdgcn_exp2f(x[u][1]);
         float a0 = x[u][0], a1 = x[u][1];
@@ -473,8 +487,10 @@ void fwd16_kernel(FwdParams p) {
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) oacc[dt] = M::run(va[h][dt], pf, oacc[dt]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);  // the V^T transpose reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
+        if constexpr (!kHoistV) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDT, 0);  // the V^T transpose reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);  // then this sub-tile's products
+        }
       }
       if (!tested) {
         calm = __any(tsum > kSlackSum) ? 0 : calm + 1;
