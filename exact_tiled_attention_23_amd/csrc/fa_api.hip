@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 
@@ -66,6 +67,58 @@ struct Split {
   float* part_lse = nullptr;
 };
 
+// Workgroups of kernel `fn` (launched with `threads` threads) that one XCD of the stream's GPU
+// holds at once: its compute units (the GPU's, over 8 XCDs) times the kernel's occupancy. Both
+// are queried once and kept.
+constexpr int kXcds = 8;
+constexpr int kMaxDevicesCached = 64;
+int slots_per_xcd(hipStream_t stream, const void* fn, int threads) {
+  static std::atomic<int> cus_of[kMaxDevicesCached];
+  struct Occ { const void* fn; int threads, blocks; };
+  static Occ occ[64];
+  static int n_occ = 0;
+  static std::mutex mu;
+  int dev = 0;
+  int cus = 256;
+  if (hipStreamGetDevice(stream, &dev) == hipSuccess && dev >= 0 && dev < kMaxDevicesCached) {
+    cus = cus_of[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+      cus_of[dev].store(cus, std::memory_order_relaxed);
+    }
+  }
+  int blocks = 1;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    int i = 0;
+    while (i < n_occ && !(occ[i].fn == fn && occ[i].threads == threads)) ++i;
+    if (i < n_occ) {
+      blocks = occ[i].blocks;
+    } else {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, threads, 0) != hipSuccess || blocks <= 0) blocks = 1;
+      if (n_occ < 64) occ[n_occ++] = Occ{fn, threads, blocks};
+    }
+  }
+  return std::max(1, cus / kXcds) * blocks;
+}
+
+// Heads per rank-by-rank group of the causal work order (unit_slot). At least as many as keep
+// two [N, D] operands per head (K and V for the forward and dQ kernels, Q and dO for the dK/dV
+// kernel) within the 4 MB L2 of an XCD, and at least as many as give the last group of an XCD
+// about twice its workgroup slots in units (a head's units average half its longest, so the
+// last group's longest unit, which starts when that group does, still ends with the rest).
+// The XCD's `hx` heads then go in groups of near-equal size, none below that.
+constexpr int64_t kL2BytesPerXcd = 4 << 20;
+int rank_group(int64_t heads, int64_t N, int64_t D, int64_t elt, int64_t per_head, int slots) {
+  const int64_t hx = std::max<int64_t>(1, heads / kXcds);
+  const int64_t head_bytes = 2 * N * D * elt;
+  const int64_t g_l2 = head_bytes > 0 ? kL2BytesPerXcd / head_bytes : hx;
+  const int64_t g_tail = (2 * (int64_t)slots + per_head - 1) / std::max<int64_t>(1, per_head);
+  const int64_t g_min = std::max<int64_t>(1, std::max(g_l2, g_tail));
+  const int64_t groups = std::max<int64_t>(1, hx / g_min);
+  return (int)std::min<int64_t>(hx, (hx + groups - 1) / groups);
+}
+
 template <typename T, int D, typename S>
 int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
                  const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
@@ -100,6 +153,7 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
   p.part_lse = sp.part_lse;
   void* args[] = {&p};
   const void* fn = sp.n > 1 ? fwd_kernel_ptr<T, D, S, true>() : fwd_kernel_ptr<T, D, S, false>();
+  p.tm_group = causal ? rank_group(B * H, N, D, sizeof(T), n_qtiles * sp.n, slots_per_xcd(stream, fn, threads)) : 1;
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -136,6 +190,7 @@ int launch_wsplit(const void* Q, const void* K, const void* V, void* O, float* L
   if (units > INT32_MAX) return FA_ERR_SHAPE;
   p.n_qtiles = (int)n_blocks;
   p.n_units = units;
+  p.tm_group = 1;  // (never more than 64 units here: one group whatever the order)
   p.n_splits = 1;
   p.BH = B * H;
   p.part_o = nullptr;
@@ -405,17 +460,17 @@ int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipSt
   p.n_tiles = (int)tiles;
   p.n_units = units;
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>),
-                                 dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
+  const void* dq_fn = reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>);
+  p.tm_group = p.causal ? rank_group(B * H, N, D, sizeof(T), tiles, slots_per_xcd(stream, dq_fn, 64 * kBwdWaves)) : 1;
+  hipError_t e = hipLaunchKernel(dq_fn, dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
-  if constexpr (D >= 96) {
-    // K/V in LDS, eight waves (two per key group): two waves per SIMD at these head dimensions.
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>),
-                        dim3((unsigned)units), dim3(64 * 8), args, 0, stream);
-  } else {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>),
-                        dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
-  }
+  // K/V in LDS, eight waves (two per key group) at D >= 96: two waves per SIMD there.
+  constexpr int kv_threads = D >= 96 ? 64 * 8 : 64 * kBwdWaves;
+  const void* kv_fn;
+  if constexpr (D >= 96) kv_fn = reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>);
+  else kv_fn = reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>);
+  p.tm_group = p.causal ? rank_group(B * H, N, D, sizeof(T), tiles, slots_per_xcd(stream, kv_fn, kv_threads)) : 1;
+  e = hipLaunchKernel(kv_fn, dim3((unsigned)units), dim3(kv_threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

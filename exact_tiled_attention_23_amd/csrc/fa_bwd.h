@@ -70,6 +70,7 @@ struct BwdParams {
   int causal;
   int n_tiles;        // query tiles (dQ kernel) or key tiles (dK/dV kernel) per head
   int64_t n_units;    // B * H * n_tiles
+  int tm_group;       // heads per rank-by-rank group (unit_slot), >= 1
 };
 
 constexpr int kStatRows = 64;  // rows per block of the stats array
@@ -87,7 +88,7 @@ __device__ __forceinline__ int decode_tile(const BwdParams& p, int bid, int* bh)
   // a head's tiles on one XCD, longest first (fa_fwd_kernel.h)
   const int heads = (int)(p.n_units / p.n_tiles);
   int slot, rank;
-  unit_slot(bid, p.n_units, heads, p.n_tiles, p.causal && !p.kv_len && !p.q_len, &slot, &rank);
+  unit_slot(bid, p.n_units, heads, p.n_tiles, p.causal && !p.kv_len && !p.q_len, p.tm_group, &slot, &rank);
   *bh = slot;
   if (p.kv_len || p.q_len) *bh = head_of_slot(slot, heads / (int)p.H, (int)p.H, true);
   return rank;

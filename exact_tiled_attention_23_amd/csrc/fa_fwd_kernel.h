@@ -83,6 +83,7 @@ struct FwdParams {
   int causal;
   int n_qtiles;           // ceil(N / BR)
   int64_t n_units;        // B * H * n_qtiles * n_splits (the grid size)
+  int tm_group;           // heads per rank-by-rank group (unit_slot), >= 1
   // Key-axis split: with n_splits > 1 the work unit also names a split s. A query tile
   // with T visible key tiles gives split s the tiles [s*c, min(T, (s+1)*c)), c = ceil(T/S),
   // and the epilogue stores that split's normalised partial state (O_s in float32, LSE_s)
@@ -121,20 +122,27 @@ struct Unit {
 // Head slot and rank within the head (0 first) of workgroup `bid`, for `heads` heads of
 // `per_head` units each. Each XCD takes a contiguous run of heads (xcd_unit). Within an XCD the
 // units go head by head, or, with `tile_major` and whole heads on every XCD (heads % 8 == 0),
-// rank by rank over the XCD's heads. Under the causal mask a head's units shrink from the first
-// rank to the last. Head by head, the next head's long units start behind the previous head's
-// short ones, and with few units per head the XCD's last long unit ends late; rank by rank is
-// the longest-first order. It is used only when every head has the same work (no per-batch
-// padding, since with padding the ranks of different heads are not comparable) and heads are
-// short (at most kTileMajorUnits units: with longer heads head by head is already balanced and
-// keeps fewer heads' K/V in the XCD's L2 at a time).
+// rank by rank over groups of `group` of the XCD's heads. Under the causal mask a head's units
+// shrink from the first rank to the last. Head by head, the next head's long units start behind
+// the previous head's short ones, and with few units per head the XCD's last long unit ends
+// late; rank by rank is the longest-first order. The group bounds how many heads' K/V the XCD
+// reads at once: the host sizes it so that a group's K and V fit in the XCD's L2 (rank by rank
+// over all of the XCD's heads would otherwise stream them from HBM when there are many heads).
+// It is used only when every head has the same work (no per-batch padding, since with padding
+// the ranks of different heads are not comparable) and heads are short (at most
+// kTileMajorUnits units: with longer heads head by head is already balanced).
 constexpr int kTileMajorUnits = 32;
 __device__ __forceinline__ void unit_slot(int bid, int64_t n_units, int heads, int per_head, bool tile_major,
-                                          int* slot, int* rank) {
+                                          int group, int* slot, int* rank) {
   if (tile_major && heads % 8 == 0 && per_head <= kTileMajorUnits) {
-    const int hx = heads / 8, i = bid / 8;
-    *slot = (bid % 8) * hx + i % hx;
-    *rank = i / hx;
+    const int hx = heads / 8, i = bid / 8;      // heads of this XCD, index of the unit in it
+    const int G = min(hx, max(group, 1));
+    const int gi = i / (G * per_head);          // group of the unit
+    const int h0 = gi * G;                      // its first head
+    const int gh = min(G, hx - h0);             // heads in the group (the last may hold fewer)
+    const int w = i - gi * G * per_head;        // index within the group
+    *slot = (bid % 8) * hx + h0 + w % gh;
+    *rank = w / gh;
   } else {
     const int unit = xcd_unit(bid, n_units);
     *slot = unit / per_head;
@@ -148,7 +156,7 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   const int ns = SPLIT ? p.n_splits : 1;
   const int per_head = p.n_qtiles * ns;
   int slot, rem;
-  unit_slot(bid, p.n_units, (int)p.BH, per_head, p.causal && !p.kv_len && !p.q_len, &slot, &rem);
+  unit_slot(bid, p.n_units, (int)p.BH, per_head, p.causal && !p.kv_len && !p.q_len, p.tm_group, &slot, &rem);
   u.bh = slot;
   if (p.kv_len || p.q_len) u.bh = head_of_slot(slot, (int)p.BH / (int)p.H, (int)p.H, true);  // B*H < 2^31
   u.qt = rem / ns;

@@ -1,8 +1,9 @@
 """GPU parity on the work orders the kernels choose from the problem's shape.
 
 Each XCD takes a contiguous run of heads. For a causal problem with no padding, B*H divisible by
-8 and at most 32 units per head, it takes them rank by rank (every head's longest tile first);
-otherwise head by head. Both orders must give the oracle's result; these cases sit on either
+8 and at most 32 units per head, it takes them rank by rank (every head's longest tile first),
+over groups of as many heads as keep two [N, D] operands per head in the XCD's L2; otherwise
+head by head. Both orders must give the oracle's result; these cases sit on either
 side of each condition, for the forward and for both backward kernels (whose units are query
 tiles of 128 rows for dQ and key tiles of 128 keys for dK/dV).
 """
@@ -68,3 +69,42 @@ def test_split_rank_order():
     torch.cuda.synchronize()
     ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True)
     compare(o, lse, ro, rl, "bf16", "split rank order")
+
+
+def test_forward_rank_groups():
+    """B*H = 72 heads (9 per XCD), N = 2048, D = 64: rank by rank in groups of 8 heads (two
+    [N, D] bf16 operands of 8 heads fill the 4 MB L2) plus a group of one. The same problem with
+    kv_len = N everywhere runs head by head; every unit's arithmetic is the same, so the two
+    outputs must agree bit for bit (a unit that ran twice or never shows up, the outputs being
+    prefilled with NaN). Sampled rows of three heads against the oracle."""
+    B, H, N = 9, 8, 2048
+    x = generate(B, H, N, 64, "bf16", causal=True, seed=5500)
+    say("rank groups forward")
+    o, lse = run_gpu(x)
+    o2, l2 = run_gpu(x, kv_len=np.full(B, N, dtype=np.int32))
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "rank-group order differs from head order"
+    ocpu, lcpu = o.float().cpu(), lse.cpu()
+    rows = np.array([0, 127, 128, 1000, 2047])
+    for b, h in [(0, 0), (4, 7), (8, 3)]:
+        ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
+                                  to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=True, rows=rows)
+        compare(ocpu[b:b + 1, h:h + 1, rows], lcpu[b:b + 1, h:h + 1, rows], ro, rl, "bf16", f"b={b} h={h}")
+
+
+def test_backward_rank_groups():
+    """The backward kernels' units in groups of 8 heads (B*H = 72, N = 2048, D = 64, 16 units
+    per head): bit for bit the result of the head-by-head order (kv_len = N)."""
+    B, H, N, D = 9, 8, 2048, 64
+    x = generate(B, H, N, D, "bf16", causal=True, seed=5600)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=5601)
+    dev = torch.device("cuda:0")
+    q, k, v, g = (t.to(dev) for t in (x.q, x.k, x.v, do))
+    say("rank groups backward")
+    o, lse = fa.forward(q, k, v, causal=True, scale=x.scale)
+    a = fa.backward(q, k, v, o, lse, g, causal=True, scale=x.scale)
+    kv = torch.full((B,), N, dtype=torch.int32, device=dev)
+    b = fa.backward(q, k, v, o, lse, g, causal=True, scale=x.scale, kv_len=kv)
+    torch.cuda.synchronize()
+    for name, s, t in zip(("dQ", "dK", "dV"), a, b):
+        assert not torch.isnan(s.float()).any(), f"NaN in {name}"
+        assert torch.equal(s, t), f"{name}: rank-group order differs from head order"
