@@ -283,7 +283,8 @@ def forward(q, k, v, *, causal=True, scale=None, kv_len=None, q_len=None, out=No
             ws_bytes = workspace.numel() * workspace.element_size()
             rc = fa_fwd_split(*args, n_splits, workspace.data_ptr(), ws_bytes, handle)
     _check(rc)
-    _mark_used_on(_side_stream(stream, dev), *made)
+    if made:
+        _mark_used_on(_side_stream(stream, dev), *made)
     return out, lse
 
 
@@ -316,7 +317,8 @@ def merge_states(part_o, part_lse, *, dtype=None, out=None, lse=None, stream=Non
         rc = fa_merge_states(part_o.data_ptr(), part_lse.data_ptr(), S, B, H, N, D, out.data_ptr(),
                              list(out.stride()[:3]), lse.data_ptr(), _TORCH_DTYPE[dtype], _stream_handle(stream, dev))
     _check(rc)
-    _mark_used_on(_side_stream(stream, dev), *made)
+    if made:
+        _mark_used_on(_side_stream(stream, dev), *made)
     return out, lse
 
 
@@ -376,7 +378,8 @@ def backward(q, k, v, o, lse, do, *, causal=True, scale=None, kv_len=None, q_len
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream_handle(stream, dev))
     _check(rc)
-    _mark_used_on(_side_stream(stream, dev), *made)
+    if made:
+        _mark_used_on(_side_stream(stream, dev), *made)
     return dq, dk, dv
 
 
