@@ -30,25 +30,38 @@ constexpr int kBlockKV = 64;   // keys per K/V tile
 // +5-15% at D = 32 and +2-10% at D = 64 against two waves per SIMD with 128-key tiles, -1.5%
 // on the padded, row-scaled f16 workload). D = 256 needs one wave per SIMD for its registers.
 template <int D> struct Shape16;
-template <> struct Shape16<32> { static constexpr int BC = 128, NW = 4, WPE = 3; };
-template <> struct Shape16<64> { static constexpr int BC = 64, NW = 4, WPE = 3; };
-template <> struct Shape16<96> { static constexpr int BC = 64, NW = 8, WPE = 2; };
-template <> struct Shape16<128> { static constexpr int BC = 64, NW = 8, WPE = 2; };
-template <> struct Shape16<256> { static constexpr int BC = 64, NW = 4, WPE = 1; };
+template <> struct Shape16<32> { static constexpr int BC = 128, NW = 4, WPE = 3, KG = 1; };
+template <> struct Shape16<64> { static constexpr int BC = 64, NW = 4, WPE = 3, KG = 1; };
+template <> struct Shape16<96> { static constexpr int BC = 64, NW = 8, WPE = 2, KG = 1; };
+template <> struct Shape16<128> { static constexpr int BC = 64, NW = 8, WPE = 2, KG = 1; };
+template <> struct Shape16<256> { static constexpr int BC = 64, NW = 4, WPE = 1, KG = 1; };
 constexpr int kMaxBC = 128;  // largest key tile: bounds the per-lane 32-bit copy offsets
 // Narrower workgroups for small causal problems at D = 96 and 128: four waves (128 query rows)
 // instead of eight. Causal query tiles differ in length, and smaller ones balance better over
 // the CUs; measured +7-17% below 2048 tiles of 256 rows, -3% at 2048, and slower without the
 // causal mask at every size tried.
-struct Shape16Narrow { static constexpr int BC = 64, NW = 4, WPE = 2; };
+struct Shape16Narrow { static constexpr int BC = 64, NW = 4, WPE = 2, KG = 1; };
 constexpr int64_t kNarrowBelowUnits = 2048;
-struct ShapeF32 { static constexpr int BC = kBlockKV, NW = kWaves; };
+// Key groups at D = 64: three groups of four waves share each 128-row query tile, each group
+// walking a third of its key tiles, and merge their partial states through LDS at the end. A
+// 12-wave workgroup fills its CU, so tiles run about 7% slower than in three 4-wave workgroups,
+// but the longest query tile finishes three times sooner. That pays only where the longest
+// tile decides the run time: causal problems without padding (whose tiles' lengths the host
+// knows) whose longest query tile has between kGroupsMinTiles and kGroupsMaxTiles key tiles and
+// exceeds the average work per workgroup slot by kGroupsTailRatio. Measured: B1 H16 N8192
+// causal +10..14%; B4 H16 N2048 causal -23% (tiles too short for the merge to pay); B1 H8
+// N16384 causal -1% (the same tail ratio, but the longer tiles already balance).
+struct Shape16Groups { static constexpr int BC = 64, NW = 4, WPE = 3, KG = 3; };
+constexpr int64_t kGroupsMinTiles = 96;
+constexpr int64_t kGroupsMaxTiles = 160;
+constexpr double kGroupsTailRatio = 1.3;
+struct ShapeF32 { static constexpr int BC = kBlockKV, NW = kWaves, KG = 1; };
 template <typename T, int D> struct DefaultShape { using type = Shape16<D>; };
 template <int D> struct DefaultShape<float, D> { using type = ShapeF32; };
 
 template <typename T, int D, typename S, bool SPLIT> const void* fwd_kernel_ptr() {
   if constexpr (sizeof(T) == 2) {
-    return reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, SPLIT>);
+    return reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, SPLIT, S::KG>);
   } else {
     return reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, S::BC, S::NW>);  // decodes splits itself
   }
@@ -125,7 +138,7 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
                  hipStream_t stream, const Split& sp) {
   constexpr int NW = S::NW;
   constexpr int BR = 32 * NW;
-  constexpr int threads = 64 * NW;
+  constexpr int threads = 64 * NW * S::KG;
   fa::FwdParams p;
   p.q = Q;
   p.k = K;
@@ -201,6 +214,19 @@ int launch_wsplit(const void* Q, const void* K, const void* V, void* O, float* L
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Whether the longest causal query tile (128 rows, 64-key tiles) outlasts the average work per
+// workgroup slot enough for the key-group kernel (Shape16Groups) to win.
+bool use_key_groups(int64_t B, int64_t H, int64_t N, hipStream_t stream) {
+  const int64_t longest = (N + 63) / 64;
+  if (longest < kGroupsMinTiles || longest > kGroupsMaxTiles) return false;
+  const int64_t qtiles = (N + 127) / 128;
+  int64_t tiles = 0;  // key tiles of one head's query tiles
+  for (int64_t i = 0; i < qtiles; ++i) tiles += (std::min<int64_t>(N, 128 * (i + 1)) + 63) / 64;
+  const void* fn = reinterpret_cast<const void*>(&fa::fwd16_kernel<__bf16, 64, 64, 4, 3, false, 1>);
+  const double slots = (double)slots_per_xcd(stream, fn, 64 * 4) * kXcds;
+  return (double)longest >= kGroupsTailRatio * (double)(B * H * tiles) / slots;
+}
+
 template <typename T, int D>
 int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H, int64_t N,
            const Strides& st, float scale, int causal, const int32_t* q_len, const int32_t* kv_len,
@@ -208,6 +234,12 @@ int launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   if constexpr (sizeof(T) == 4) {
     if (sp.n == 1 && B * H * ((N + 127) / 128) <= kWaveSplitMaxTiles)
       return launch_wsplit<T, D>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream);
+  }
+  if constexpr (sizeof(T) == 2 && D == 64) {
+    if (sp.n == 1 && causal && !kv_len && !q_len && use_key_groups(B, H, N, stream)) {
+      return launch_shape<T, D, Shape16Groups>(Q, K, V, O, LSE, B, H, N, st, scale, causal, q_len, kv_len, stream,
+                                                sp);
+    }
   }
   if constexpr (sizeof(T) == 2 && (D == 96 || D == 128)) {
     static_assert(Shape16<D>::NW == 8, "the narrow shape halves an 8-wave workgroup");

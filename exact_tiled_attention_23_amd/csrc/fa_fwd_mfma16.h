@@ -127,8 +127,8 @@ template <int D> __device__ __forceinline__ int swz_v(int j) {
 // last four 16-byte chunks are never copied nor read.
 template <int D> constexpr int lds_cols() { return D == 96 ? 128 : D; }
 
-template <typename T, int D, int BC, int NW, int WPE, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+template <typename T, int D, int BC, int NW, int WPE, bool SPLIT, int KG = 1>
+__global__ __launch_bounds__(NW * KG * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -149,11 +149,21 @@ void fwd16_kernel(FwdParams p) {
   constexpr int NDT = D / 32;
   constexpr int NQF = D / 16;
   static_assert(BLOCKS % NW == 0, "tile must split evenly over waves");
+  static_assert(KG >= 1 && KG <= 4, "key groups");
+  constexpr int GROUPB = 2 * 2 * TILEB;          // LDS bytes of one key group's two buffers
+  // Partial states of key groups 1..KG-1 for the merge: per wave, NDT*16 accumulators and the
+  // reference and sum, element-major over the 64 lanes.
+  constexpr int STATEF = NDT * 16 + 2;
+  static_assert(KG == 1 || (KG - 1) * NW * 64 * STATEF * 4 <= KG * GROUPB, "merge area fits in LDS");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * TILEB];  // [buf][K|V][tile]
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[KG * GROUPB];  // [group][buf][K|V][tile]
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  // Waves NW*k .. NW*k + NW-1 form key group k: group k takes the k-th of KG equal runs of
+  // the unit's key tiles, each wave of it the same 32 query rows as wave w % NW of every group.
+  const int kgrp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / NW);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) % NW);   // wave-uniform
+  const unsigned gbase = (unsigned)kgrp * GROUPB;  // this group's buffers
   const int g = lane >> 5;
   const int r = lane & 31;
 
@@ -207,8 +217,13 @@ void fwd16_kernel(FwdParams p) {
   const int all_tiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
   const int ns = SPLIT ? p.n_splits : 1;
   const int chunk = (all_tiles + ns - 1) / ns;
-  const int t_lo = min(all_tiles, wu.split * chunk);
-  const int t_hi = min(all_tiles, t_lo + chunk);
+  const int u_lo = min(all_tiles, wu.split * chunk);
+  const int u_hi = min(all_tiles, u_lo + chunk);
+  // This key group's run [t_lo, t_hi) of them. Every group passes the barriers of `steps`
+  // tiles (a group with a shorter run idles through its last ones).
+  const int steps = (u_hi - u_lo + KG - 1) / KG;
+  const int t_lo = min(u_hi, u_lo + kgrp * steps);
+  const int t_hi = min(u_hi, t_lo + steps);
 
   // ---- per-lane constants of the global -> LDS copies: block blk = wave*LPW + i holds
   // rows blk*RPB .. +RPB-1; this lane fills the block's 16-byte slot `lane`, i.e. physical
@@ -233,7 +248,7 @@ void fwd16_kernel(FwdParams p) {
     constexpr int buf = decltype(buf_c)::value;
     const unsigned char* kt = Kh + (int64_t)j0 * ksnb;
     const unsigned char* vt = Vh + (int64_t)j0 * vsnb;
-    unsigned char* kb = lds + buf * 2 * TILEB;
+    unsigned char* kb = lds + gbase + buf * 2 * TILEB;
     unsigned char* vb = kb + TILEB;
     const unsigned kl = lds_address(kb), vl = lds_address(vb);
     if (j0 + BC <= n) {
@@ -273,13 +288,13 @@ void fwd16_kernel(FwdParams p) {
   const int kr = a_row_key<8>(r);                 // K row this lane feeds as A-operand row r
   int koff[NQF];
 #pragma unroll
-  for (int s = 0; s < NQF; ++s) koff[s] = kr * ROWB + ((2 * s + g) ^ swz_k<DL>(kr)) * 16;
+  for (int s = 0; s < NQF; ++s) koff[s] = gbase + kr * ROWB + ((2 * s + g) ^ swz_k<DL>(kr)) * 16;
   const int s16 = lane & 15, s4 = s16 >> 2, sm = s16 & 3, q2 = (lane >> 4) & 1;
   int voff[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     const int c = 4 * dt + 2 * q2 + (sm >> 1);
-    voff[dt] = (8 * g + s4) * ROWB + ((c ^ swz_v<DL>(s4)) * 16) + (sm & 1) * 8;
+    voff[dt] = gbase + (8 * g + s4) * ROWB + ((c ^ swz_v<DL>(s4)) * 16) + (sm & 1) * 8;
   }
 
   f32x16 oacc[NDT];
@@ -315,21 +330,21 @@ void fwd16_kernel(FwdParams p) {
     const unsigned char* kb = lds + buf * 2 * TILEB;
     const unsigned char* vb = kb + TILEB;
     wait_vmem();  // this wave's copies of tile t have landed
-    if (j0 + BC > kvl) {
+    if ((KG == 1 || t < t_hi) && j0 + BC > kvl) {
       // Padding rows (key >= kv_len) of V must not carry garbage into O: zero the slots
       // this lane filled itself.
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         if (j0 + ld_row[i] >= kvl) {
           const int blk = wave * LPW + i;
-          *reinterpret_cast<uint4*>(lds + buf * 2 * TILEB + TILEB + blk * 1024 + lane * 16) = uint4{0, 0, 0, 0};
+          *reinterpret_cast<uint4*>(lds + gbase + buf * 2 * TILEB + TILEB + blk * 1024 + lane * 16) = uint4{0, 0, 0, 0};
         }
       }
     }
     __syncthreads();  // tile t visible to all waves; all waves are done with tile t-1
     if (t + 1 < t_hi) issue_tile(j0 + BC, Int<buf ^ 1>{});
 
-    if (j0 < wave_hi) {
+    if ((KG == 1 || t < t_hi) && j0 < wave_hi) {
       // ---- S^T = K . Q^T. The sub-tiles' products advance together, one reduction step
       // at a time, and the K fragments of step st+PD are read while step st's products run,
       // so each LDS read has about four products' time (~128 cycles) to land. The order is
@@ -500,14 +515,14 @@ void fwd16_kernel(FwdParams p) {
   };
   auto tile_loop = [&]() __attribute__((always_inline)) {
     if (t_lo < t_hi) issue_tile(t_lo * BC, Int<0>{});
-    for (int t = t_lo; t < t_hi; t += 2) {
-      tile_step(t, Int<0>{});
-      if (t + 1 >= t_hi) break;
-      tile_step(t + 1, Int<1>{});
+    for (int i = 0; i < steps; i += 2) {
+      tile_step(t_lo + i, Int<0>{});
+      if (i + 1 >= steps) break;
+      tile_step(t_lo + i + 1, Int<1>{});
     }
   };
   tile_loop();
-  if (t_lo < t_hi && *static_cast<volatile int*>(&overflow_flag)) {
+  if (steps > 0 && *static_cast<volatile int*>(&overflow_flag)) {
     __syncthreads();  // every wave is done with the tiles, so the buffers can be refilled
     test_all = true;
     calm = 0;
@@ -517,6 +532,40 @@ void fwd16_kernel(FwdParams p) {
     nmuse = 0.f;
     lsum = 0.f;
     tile_loop();
+  }
+
+  // ---- merge of the key groups' partial states into group 0 (the monoid of (m, l, O) pairs:
+  // the larger reference, and each state's sum and accumulators brought to it).
+  if constexpr (KG > 1) {
+    __syncthreads();  // every wave is done with the tiles; the merge area overlays them
+    float* area = reinterpret_cast<float*>(lds);
+    if (kgrp > 0) {
+      float* st = area + ((kgrp - 1) * NW + wave) * (64 * STATEF);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[(dt * 16 + i) * 64 + lane] = oacc[dt][i];
+      st[(NDT * 16) * 64 + lane] = mref;
+      st[(NDT * 16 + 1) * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (kgrp > 0) return;
+#pragma unroll
+    for (int k = 1; k < KG; ++k) {
+      const float* st = area + ((k - 1) * NW + wave) * (64 * STATEF);
+      const float mk = st[(NDT * 16) * 64 + lane];
+      const float lk = st[(NDT * 16 + 1) * 64 + lane];
+      const float m = fmaxf(mref, mk);
+      // A state that has seen no key (reference -inf, sum and accumulators 0) weighs nothing.
+      const float a = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - m);
+      const float bk = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - m);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = oacc[dt][i] * a + st[(dt * 16 + i) * 64 + lane] * bk;
+      lsum = lsum * a + lk * bk;
+      mref = m;
+    }
   }
 
   // ---- epilogue

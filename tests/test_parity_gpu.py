@@ -462,3 +462,34 @@ def test_untested_probability_near_float16_limit(dtype, D, causal):
         o, lse = run_gpu(x)
         ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal)
         compare(o, lse, ro, rl, dtype, f"probability 2^{lg}")
+
+
+# ---------------------------------------------------------------- key groups (long causal, D = 64)
+@pytest.mark.parametrize("dtype,N,H", [("bf16", 8192, 2), ("f16", 7000, 3)])
+def test_key_groups_long_causal(dtype, N, H):
+    """Causal D = 64 with few heads and long query tiles takes the key-group kernel: three
+    groups of waves split each query tile's key tiles and merge their partial states. Every
+    element against the oracle (ragged N included), with a NaN prefill and a determinism check."""
+    x = generate(1, H, N, 64, dtype, causal=True, seed=3700 + N)
+    say(f"key groups {dtype} N={N} H={H}")
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True, workers=oracle_workers())
+    compare(o, lse, ro, rl, dtype, f"key groups N={N}")
+    o2, l2 = run_gpu(x)
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "not deterministic"
+
+
+def test_key_groups_reference_jump():
+    """A key whose logit stands 40 (base 2) above the rest, late in a long causal row, under the
+    key-group kernel: the group that holds it overflows its untested sum and the whole workgroup
+    takes the all-tested pass; the merge then weighs the groups by their references."""
+    N = 8192
+    c = float(np.float32(1.0 / np.sqrt(64))) * 1.4426950408889634
+    x = generate(1, 2, N, 64, "bf16", causal=True, seed=3800)
+    x.q[..., -1] = 1.0
+    x.k[..., -1] = 0.0
+    x.k[:, :, 6000, -1] = 40.0 / c
+    say("key groups reference jump")
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True, workers=oracle_workers())
+    compare(o, lse, ro, rl, "bf16", "key groups jump")
