@@ -35,9 +35,10 @@ METRIC_BWD = "attn bwd TFLOP/s (5 products of 2D flops per pair) and % bf16 MFMA
 # MI355X published dense matrix peaks, TFLOP/s, and HBM3E bandwidth, GB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["exact_tiled_attention_23_amd/csrc/fa_fwd_kernel.h", "exact_tiled_attention_23_amd/csrc/fa_fwd_mfma16.h",
-                  "exact_tiled_attention_23_amd/csrc/fa_merge.h", "exact_tiled_attention_23_amd/csrc/fa_bwd.h",
-                  "exact_tiled_attention_23_amd/csrc/fa_api.hip"]
+# Every source file the library is compiled from (a counter record is current only for them).
+KERNEL_SOURCES = sorted(os.path.join("exact_tiled_attention_23_amd", "csrc", f)
+                        for f in os.listdir(os.path.join(ROOT, "exact_tiled_attention_23_amd", "csrc"))
+                        if f.endswith((".h", ".hip")))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -171,8 +172,9 @@ def main():
                     help="(batch, head) pairs the CPU oracle baseline runs; all of the headline workload by default")
     ap.add_argument("--backward", action="store_true", help="time the backward (fa_bwd) instead of the forward")
     ap.add_argument("--shape", default=None,
-                    help="B,H,N,D,dtype,causal: a seeded synthetic workload of this shape instead of a named one "
-                         "(the recipe of the named workloads, seed 7)")
+                    help="B,H,N,D,dtype,causal[,padded][,rowscale]: a seeded synthetic workload of this shape "
+                         "instead of a named one (the recipe of the named workloads, seed 7); 'padded' draws a "
+                         "kv_len per batch element, 'rowscale' scales each query row by a factor in [1, 100]")
     ap.add_argument("--cold-bytes", type=int, default=0,
                     help="write this many bytes of scratch memory between timed launches (e.g. 1 GiB, beyond the "
                          "256 MB MALL) so each launch finds its inputs outside the caches; value is then the "
@@ -233,10 +235,13 @@ def main():
         return
 
     if args.shape:
-        B, H, N, D, dt, causal = args.shape.split(",")
-        causal = causal.strip().lower() in ("1", "true", "causal")
-        name = f"b{B}h{H}n{N}d{D}-{dt}" + ("-causal" if causal else "")
-        w = Workload(name, int(B), int(H), int(N), int(D), dt, causal, seed=7)
+        fields = [f.strip().lower() for f in args.shape.split(",")]
+        B, H, N, D, dt, causal = fields[:6]
+        causal = causal in ("1", "true", "causal")
+        padded, rowscale = "padded" in fields[6:], "rowscale" in fields[6:]
+        name = (f"b{B}h{H}n{N}d{D}-{dt}" + ("-causal" if causal else "") + ("-padded" if padded else "")
+                + ("-rowscale" if rowscale else ""))
+        w = Workload(name, int(B), int(H), int(N), int(D), dt, causal, padding=padded, q_row_scale=rowscale, seed=7)
     else:
         name = args.workload or HEADLINE
         w = WORKLOADS[name]
