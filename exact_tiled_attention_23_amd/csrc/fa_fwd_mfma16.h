@@ -312,11 +312,14 @@ void fwd16_kernel(FwdParams p) {
   // above 2^slack only makes the next tile test again (the probabilities are exact for any
   // reference while nothing overflows); a sum above kUntestedSumBound (or infinite, or NaN) is an
   // overflow, and the whole workgroup then computes its unit again with every tile tested.
+  // A wave whose reference moves a second time (a row's maximum rising past the slack after its
+  // first valid key) tests every later tile of the unit: rows whose logits spread that widely
+  // (queries of very different norms, say) would keep overflowing untested tiles.
   // The last key tile of the unit is always tested, so every wave has reported an overflow
   // (one LDS word, cleared before the first tile's barrier) before the barrier of that tile, and
   // after the loop every wave reads the same word without another barrier.
   int calm = 0;              // wave-uniform: tiles since the reference last moved
-  bool test_all = false;     // the second pass, after an overflow
+  bool test_all = false;     // wave-uniform: the second pass, or a reference that moved twice
   __shared__ int overflow_flag;
   if (threadIdx.x == 0) overflow_flag = 0;
 
@@ -454,6 +457,7 @@ void fwd16_kernel(FwdParams p) {
       // Move the reference when some row's maximum rose more than the slack above it, or when
       // a row sees its first valid key (its reference is still -inf).
       calm = calm + 1;
+      if (__any((mx > kRescaleSlack) & (mref != -INFINITY))) test_all = true;
       if (__any((mx > kRescaleSlack) | ((mref == -INFINITY) & (mx != -INFINITY)))) {
         calm = 0;
         const float mnew = fmaxf(mref, mx - nmuse);
