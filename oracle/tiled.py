@@ -1,33 +1,55 @@
-"""The pages' tiled forward pass with online softmax, in float64.
+"""The tiled forward pass with online softmax, in float64, as merges of per-block partial states.
 
 TEST INFRASTRUCTURE (see the package docstring): never imported by the
 product path.
 
-What this model is: the recurrence the GPU kernel runs, kept in float64, so that
-it must reach the naive definition up to the order of rounding. The method it
-follows is the one of "vectorized-flash-attention-kernel" (Core algorithm; Key
-design decisions 1, 3 and 4) and "js-flash-attention-tiled-online-softmax-
-exactness" (Root causes addressed 1 and 2).
+What this model is: the computation the GPU kernel runs, block by block, kept in
+float64, so that it must reach the naive definition up to the order of rounding.
+The pages describe it as a running per-row state updated by each key block
+("vectorized-flash-attention-kernel", Core algorithm; Key design decisions 1 and
+3; "js-flash-attention-tiled-online-softmax-exactness", Root causes addressed 1
+and 2), and the course module names the structure behind that update: partial
+softmax states form a monoid ("Paper: FlashAttention", Objectives, Math & data
+structures). This model is written in the second form.
 
-In short: every query row carries a small state while the key blocks go by, its
-largest scaled logit so far, the sum of its exponentials taken relative to that
-largest value, and the matching weighted sum of value rows. A new key block
-contributes its own exponentials; when it raises the row's largest logit, the
-state held so far is first brought to the new reference by one exponential
-factor, which keeps every exponential at most 1 and so nothing overflows. A key
-after the query (causal mask) or at or past kv_len contributes nothing. A row
-that has not yet seen a valid key keeps the empty state, so the factor is never
-formed from two infinities. At the end the weighted sum is divided by the sum
-(exact zeros for an empty row, whose sum is exactly zero) and the two row
-statistics are returned folded into one number, LSE = largest logit + ln(sum).
+A partial state of one query row over a set of keys is a triple (m, l, a): m is
+the largest scaled logit among the keys, l the sum of exp(logit - m) over them,
+and a the same sum with each term multiplying the key's value row. The empty set
+has (-inf, 0, 0). Two states merge into the state of the union by bringing both
+to the larger of the two m, each scaled by exp(its m - the larger m), and adding
+l and a. The merge is associative, so walking the key blocks in order and
+merging each block's own state into the running one gives the state of all keys,
+whatever the block size. An empty block or an empty running state has m = -inf;
+its scale factor is taken as 0, never formed from two infinities. At the end the
+row's output is a / l (exact zeros when l is zero: the row saw no key) and its
+LSE is m + ln(l).
 
-A key/value block is skipped when it lies wholly in the future of the query
+Keys after the query (causal mask) or at or past kv_len belong to no block's
+state. A key block is skipped when it lies wholly in the future of the query
 block (its first key index exceeds the block's last query index), and blocks
 wholly past every batch's kv_len are skipped too. All (b, h) are processed at
 once with array arithmetic; the two loops are the block loops.
 """
 
 import numpy as np
+
+
+def _block_state(s, valid, v_block):
+    """Partial state (m, l, a) of each row over one key block: s the scaled logits [B,H,R,C],
+    valid the visible keys, v_block [B,H,C,Dv]."""
+    m = np.max(np.where(valid, s, -np.inf), axis=-1)
+    seen = m > -np.inf
+    w = np.where(valid, np.exp(s - np.where(seen, m, 0.0)[..., None]), 0.0)
+    return m, w.sum(axis=-1), np.matmul(w, v_block)
+
+
+def _merge(m1, l1, a1, m2, l2, a2):
+    """State of the union of two disjoint key sets from their two states."""
+    m = np.maximum(m1, m2)
+    m_sub = np.where(m > -np.inf, m, 0.0)   # both empty: factors exp(-inf) = 0, not exp(nan)
+    f1 = np.exp(m1 - m_sub)
+    f2 = np.exp(m2 - m_sub)
+    return m, f1 * l1 + f2 * l2, f1[..., None] * a1 + f2[..., None] * a2
 
 
 def tiled_attention(q, k, v, scale, causal=False, kv_len=None, block_q=64, block_kv=64):
@@ -47,7 +69,7 @@ def tiled_attention(q, k, v, scale, causal=False, kv_len=None, block_q=64, block
         rows = np.arange(q0, q1)
         m = np.full((B, H, q1 - q0), -np.inf)
         l = np.zeros((B, H, q1 - q0))
-        acc = np.zeros((B, H, q1 - q0, Dv))
+        a = np.zeros((B, H, q1 - q0, Dv))
         for k0 in range(0, N, block_kv):
             k1 = min(k0 + block_kv, N)
             if causal and k0 > q1 - 1:
@@ -56,20 +78,11 @@ def tiled_attention(q, k, v, scale, causal=False, kv_len=None, block_q=64, block
                 continue
             cols = np.arange(k0, k1)
             s = scale * np.matmul(q[:, :, q0:q1], np.swapaxes(k[:, :, k0:k1], -1, -2))
-            masked = cols[None, None, None, :] >= L[:, None, None, None]
+            valid = cols[None, None, None, :] < L[:, None, None, None]
             if causal:
-                masked = masked | (cols[None, :] > rows[:, None])[None, None]
-            s = np.where(masked, -np.inf, s)
-            m_new = np.maximum(m, s.max(axis=-1))
-            live = m_new > -np.inf
-            m_sub = np.where(live, m_new, 0.0)
-            correction = np.where(live, np.exp(m - m_sub), 1.0)
-            p = np.exp(s - m_sub[..., None])
-            l = correction * l + p.sum(axis=-1)
-            acc = correction[..., None] * acc + np.matmul(p, v[:, :, k0:k1])
-            m = m_new
-        has = ~(l == 0)
-        safe_l = np.where(has, l, 1.0)
-        o[:, :, q0:q1] = np.where(has[..., None], acc / safe_l[..., None], 0.0)
-        lse[:, :, q0:q1] = np.where(has, m + np.log(safe_l), -np.inf)
+                valid = valid & (cols[None, :] <= rows[:, None])[None, None]
+            m, l, a = _merge(m, l, a, *_block_state(s, valid, v[:, :, k0:k1]))
+        seen = l != 0   # exactly when the row saw no key (a NaN from a slip stays visible)
+        o[:, :, q0:q1] = np.where(seen[..., None], a / np.where(seen, l, 1.0)[..., None], 0.0)
+        lse[:, :, q0:q1] = np.where(seen, m + np.log(np.where(seen, l, 1.0)), -np.inf)
     return o, lse

@@ -84,16 +84,20 @@ def test_query_padding_mutant_is_caught(name):
 
 
 TILED_MUTANTS = {
-    "no-rescale-l": ("l = correction * l + p.sum(axis=-1)", "l = l + p.sum(axis=-1)"),
-    "no-rescale-acc": ("acc = correction[..., None] * acc + np.matmul(p, v[:, :, k0:k1])",
-                       "acc = acc + np.matmul(p, v[:, :, k0:k1])"),
-    "causal-mask-ge": ("(cols[None, :] > rows[:, None])", "(cols[None, :] >= rows[:, None])"),
-    "no-inf-guard": ("m_sub = np.where(live, m_new, 0.0)", "m_sub = m_new"),
-    "normalise-in-loop": ("            m = m_new\n",
-                          "            m = m_new; acc = acc / np.where(l > 0, l, 1.0)[..., None]\n"),
+    "no-rescale-l": ("f1 * l1 + f2 * l2", "l1 + f2 * l2"),
+    "no-rescale-acc": ("f1[..., None] * a1 + f2[..., None] * a2", "a1 + f2[..., None] * a2"),
+    "causal-mask-drops-diagonal": ("(cols[None, :] <= rows[:, None])", "(cols[None, :] < rows[:, None])"),
+    "no-inf-guard": ("m_sub = np.where(m > -np.inf, m, 0.0)", "m_sub = m"),
+    "normalise-in-loop": ("            m, l, a = _merge(m, l, a, *_block_state(s, valid, v[:, :, k0:k1]))\n",
+                          "            m, l, a = _merge(m, l, a, *_block_state(s, valid, v[:, :, k0:k1]))\n"
+                          "            a = a / np.where(l > 0, l, 1.0)[..., None]\n"),
     "skip-diagonal-block": ("if causal and k0 > q1 - 1:", "if causal and k0 >= q1 - 1:"),
-    "correction-sign": ("np.exp(m - m_sub)", "np.exp(m_sub - m)"),
-    "stale-max": ("            m = m_new\n", "            pass\n"),
+    "correction-sign": ("f1 = np.exp(m1 - m_sub)", "f1 = np.exp(m_sub - m1)"),
+    "stale-max": ("return m, f1 * l1", "return m1, f1 * l1"),
+    "masked-keys-weighted": ("w = np.where(valid, np.exp(s - np.where(seen, m, 0.0)[..., None]), 0.0)",
+                             "w = np.exp(s - np.where(seen, m, 0.0)[..., None])"),
+    "padding-ignored": ("valid = cols[None, None, None, :] < L[:, None, None, None]",
+                        "valid = cols[None, None, None, :] < N"),
 }
 
 
