@@ -39,7 +39,7 @@ def _block_state(s, valid, v_block):
     valid the visible keys, v_block [B,H,C,Dv]."""
     m = np.max(np.where(valid, s, -np.inf), axis=-1)
     seen = m > -np.inf
-    w = np.where(valid, np.exp(s - np.where(seen, m, 0.0)[..., None]), 0.0)
+    w = np.exp(np.where(valid, s - np.where(seen, m, 0.0)[..., None], -np.inf))
     return m, w.sum(axis=-1), np.matmul(w, v_block)
 
 

@@ -94,8 +94,8 @@ TILED_MUTANTS = {
     "skip-diagonal-block": ("if causal and k0 > q1 - 1:", "if causal and k0 >= q1 - 1:"),
     "correction-sign": ("f1 = np.exp(m1 - m_sub)", "f1 = np.exp(m_sub - m1)"),
     "stale-max": ("return m, f1 * l1", "return m1, f1 * l1"),
-    "masked-keys-weighted": ("w = np.where(valid, np.exp(s - np.where(seen, m, 0.0)[..., None]), 0.0)",
-                             "w = np.exp(s - np.where(seen, m, 0.0)[..., None])"),
+    "masked-keys-weighted": ("np.where(valid, s - np.where(seen, m, 0.0)[..., None], -np.inf)",
+                             "s - np.where(seen, m, 0.0)[..., None]"),
     "padding-ignored": ("valid = cols[None, None, None, :] < L[:, None, None, None]",
                         "valid = cols[None, None, None, :] < N"),
 }
