@@ -92,12 +92,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
   if (q0 >= nq) kv_hi = 0;
   const int n_tiles = kv_hi > 0 ? (int)((kv_hi + BC - 1) / BC) : 0;
 
-  frag qf[NQF];
+  // ---- the block's 32 Q rows, loaded with 16-byte row chunks (coalesced; a float32 fragment is
+  // one element per lane, so loading fragments directly would touch 32 rows per instruction)
+  // and read back from this wave's K staging region in the B-operand layout below.
+  uint4 qreg[K_UNITS];
 #pragma unroll
-  for (int s = 0; s < NQF; ++s) {
-    if (qrow < nq) qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + KSTEP * s + KPER * g);
-    else qf[s] = frag{};
+  for (int n = 0; n < K_UNITS; ++n) {
+    const int cidx = lane + n * 64;
+    const int64_t qr = q0 + cidx / CPR;
+    qreg[n] = qr < nq ? *reinterpret_cast<const uint4*>(Qh + qr * qsn + (cidx % CPR) * CH) : uint4{0, 0, 0, 0};
   }
+  frag qf[NQF];
 
   f32x16 oacc[NDT];
 #pragma unroll
@@ -159,8 +164,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
     }
   };
 
+#pragma unroll
+  for (int n = 0; n < K_UNITS; ++n) {
+    const int cidx = lane + n * 64;
+    *reinterpret_cast<uint4*>(&k_lds[(cidx / CPR) * KLD + (cidx % CPR) * CH]) = qreg[n];
+  }
   int t = wave;
-  if (t < n_tiles) load_tile((int64_t)t * BC);
+  if (t < n_tiles) load_tile((int64_t)t * BC);  // in flight while the fragments are read
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int s = 0; s < NQF; ++s)  // padding rows read zeros (their rows were not loaded)
+    qf[s] = *reinterpret_cast<const frag*>(&k_lds[r * KLD + KSTEP * s + KPER * g]);
   for (; t < n_tiles; t += NW) {
     const int64_t j0 = (int64_t)t * BC;
     // Only this wave touches its LDS region, and the LDS serves one wave's accesses in order;
