@@ -59,9 +59,9 @@ struct ShapeF32 { static constexpr int BC = kBlockKV, NW = kWaves, KG = 1; };
 template <typename T, int D> struct DefaultShape { using type = Shape16<D>; };
 template <int D> struct DefaultShape<float, D> { using type = ShapeF32; };
 
-template <typename T, int D, typename S, bool SPLIT> const void* fwd_kernel_ptr() {
+template <typename T, int D, typename S, bool SPLIT, bool LPT = false> const void* fwd_kernel_ptr() {
   if constexpr (sizeof(T) == 2) {
-    return reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, SPLIT, S::KG>);
+    return reinterpret_cast<const void*>(&fa::fwd16_kernel<T, D, S::BC, S::NW, S::WPE, SPLIT, S::KG, LPT>);
   } else {
     return reinterpret_cast<const void*>(&fa::fwd_kernel<T, D, S::BC, S::NW>);  // decodes splits itself
   }
@@ -165,7 +165,17 @@ int launch_shape(const void* Q, const void* K, const void* V, void* O, float* LS
   p.part_o = sp.part_o;
   p.part_lse = sp.part_lse;
   void* args[] = {&p};
-  const void* fn = sp.n > 1 ? fwd_kernel_ptr<T, D, S, true>() : fwd_kernel_ptr<T, D, S, false>();
+  // Key padding: each XCD runs its units longest first (decode_unit_lpt) when it holds whole
+  // heads, at most one per lane of a wave. Measured on B8 H8 N4096 D64 f16 causal with three
+  // kv_len draws: +17% to +35% against the head-by-head order.
+  const bool lpt = sizeof(T) == 2 && S::KG == 1 && kv_len && !q_len && sp.n == 1 && (B * H) % kXcds == 0 &&
+                   B * H / kXcds <= 64;
+  const void* fn = fwd_kernel_ptr<T, D, S, false>();
+  if (sp.n > 1) {
+    fn = fwd_kernel_ptr<T, D, S, true>();
+  } else if constexpr (sizeof(T) == 2 && S::KG == 1) {
+    if (lpt) fn = fwd_kernel_ptr<T, D, S, false, true>();
+  }
   p.tm_group = causal ? rank_group(B * H, N, D, sizeof(T), n_qtiles * sp.n, slots_per_xcd(stream, fn, threads)) : 1;
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -165,6 +165,82 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   return u;
 }
 
+// Work unit of workgroup `bid` for a key-padded problem (kv_len given, no q_len, no split, whole
+// heads on every XCD, at most 64 of them: the host checks all of this and then launches the
+// kernel instantiation that calls this). The work of a unit is its
+// number of key tiles, which under key padding differs between batch elements, and each XCD runs
+// its units in the order of decreasing work (ties in head-slot order, then by query tile from the
+// last), so that its longest units start first and the short ones fill the end. The host cannot
+// sort the units (kv_len lives on the device), so every wave finds its workgroup's place in that
+// order itself:
+//  * The XCD holds head slots [x*hx, (x+1)*hx) (slots run over the batch fastest, as in
+//    head_of_slot); lane s holds the kv_len of slot x*hx + s.
+//  * A head whose kv_len exceeds (t-1)*BC has per_head - floor((t-1)*BC/BR) units with at least
+//    t key tiles under the causal mask (its query tiles from that index on), and all per_head
+//    units without it; other heads have none. So the XCD's count of units with at least t tiles
+//    is that per-head count times the number of such heads (one ballot).
+//  * A binary search over t finds the work ts of the i-th unit (the largest t whose count exceeds
+//    i); the units of work exactly ts, taken head by head (a prefix sum over the lanes), give the
+//    head and, counted from its longest, the query tile.
+// All of it is wave-uniform: every wave of the workgroup finds the same unit.
+template <int BR, int BC>
+__device__ __forceinline__ Unit decode_unit_lpt(const FwdParams& p, int bid) {
+  const int heads = (int)p.BH, H = (int)p.H, B = heads / H, hx = heads / 8;
+  const int per_head = p.n_qtiles;
+  const int n = (int)p.N;
+  const bool causal = p.causal != 0;
+  const int x = bid % 8, i = bid / 8;
+  const int lane = threadIdx.x & 63;
+  int kv = -1;  // kv_len of this lane's head slot (lanes past hx hold none)
+  if (lane < hx) {
+    const int v = p.kv_len[(x * hx + lane) % B];
+    kv = v < 0 ? 0 : (v > n ? n : v);
+  }
+  // Units of a head (kv_len kvl) with at least t key tiles.
+  auto at_least = [&](int t, int kvl) {
+    if (kvl < 0) return 0;
+    if (t <= 0) return per_head;
+    if (kvl <= (t - 1) * BC) return 0;
+    return causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
+  };
+  // The same over the XCD's heads.
+  auto count_at_least = [&](int t) {
+    if (t <= 0) return hx * per_head;
+    const int per = causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
+    return per * (int)__popcll(__ballot(kv > (t - 1) * BC));
+  };
+  int lo = 0, hi = (n + BC - 1) / BC + 1;  // count_at_least(lo) > i >= count_at_least(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (count_at_least(mid) > i) lo = mid;
+    else hi = mid;
+  }
+  const int ts = lo;
+  const int j = i - count_at_least(ts + 1);  // place among the units of work exactly ts
+  const int above = at_least(ts + 1, kv);
+  const int e = at_least(ts, kv) - above;    // this head's units of work exactly ts
+  int pre = e;                                // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(pre, d);
+    if (lane >= d) pre += y;
+  }
+  const unsigned long long m = __ballot(pre > j);
+  int sl = m ? (int)__builtin_ctzll(m) : hx - 1;
+  sl = min(sl, hx - 1);
+  const int jj = j - (__shfl(pre, sl) - __shfl(e, sl));
+  const int above_s = __shfl(above, sl);
+  // The head's units of work ts are the query tiles just below those with more work.
+  int qt = (above_s > 0 ? per_head - above_s - 1 : per_head - 1) - jj;
+  qt = max(0, min(qt, per_head - 1));
+  const int slot = x * hx + sl;
+  Unit u;
+  u.bh = (slot % B) * H + slot / B;
+  u.qt = qt;
+  u.split = 0;
+  return u;
+}
+
 // Key index (within a 32-key sub-tile) held by accumulator register i of lane half g.
 // The 32x32 accumulator gives register i of half g the row 8*(i/4) + 4*g + i%4; the
 // K rows are loaded permuted so that this row holds key KSTEP*(i/KPER) + KPER*g + i%KPER,

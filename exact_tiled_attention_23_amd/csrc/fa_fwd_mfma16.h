@@ -127,7 +127,8 @@ template <int D> __device__ __forceinline__ int swz_v(int j) {
 // last four 16-byte chunks are never copied nor read.
 template <int D> constexpr int lds_cols() { return D == 96 ? 128 : D; }
 
-template <typename T, int D, int BC, int NW, int WPE, bool SPLIT, int KG = 1>
+// LPT: the key-padded launch, whose workgroups take their units longest first (decode_unit_lpt).
+template <typename T, int D, int BC, int NW, int WPE, bool SPLIT, int KG = 1, bool LPT = false>
 __global__ __launch_bounds__(NW * KG * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void fwd16_kernel(FwdParams p) {
   using M = Mma<T>;
@@ -167,7 +168,10 @@ void fwd16_kernel(FwdParams p) {
   const int g = lane >> 5;
   const int r = lane & 31;
 
-  const Unit wu = decode_unit<SPLIT>(p, blockIdx.x);
+  static_assert(!(LPT && SPLIT), "the longest-first order is for unsplit launches");
+  Unit wu;
+  if constexpr (LPT) wu = decode_unit_lpt<BR, BC>(p, blockIdx.x);
+  else wu = decode_unit<SPLIT>(p, blockIdx.x);
   const int bh = wu.bh;
   const int qt = wu.qt;
   const int b = bh / (int)p.H;

@@ -2,8 +2,10 @@
 
 Each XCD takes a contiguous run of heads. For a causal problem with no padding, B*H divisible by
 8 and at most 32 units per head, it takes them rank by rank (every head's longest tile first),
-over groups of as many heads as keep two [N, D] operands per head in the XCD's L2; otherwise
-head by head. Both orders must give the oracle's result; these cases sit on either
+over groups of as many heads as keep two [N, D] operands per head in the XCD's L2. With key
+padding only (kv_len, no q_len), B*H divisible by 8 and at most 64 heads per XCD, the forward
+takes its units longest first, an order each workgroup finds on the device; otherwise head by
+head. Both orders must give the oracle's result; these cases sit on either
 side of each condition, for the forward and for both backward kernels (whose units are query
 tiles of 128 rows for dQ and key tiles of 128 keys for dK/dV).
 """
@@ -89,6 +91,40 @@ def test_forward_rank_groups():
         ro, rl = oracle.attention(to_f64(x.q[b:b + 1, h:h + 1]), to_f64(x.k[b:b + 1, h:h + 1]),
                                   to_f64(x.v[b:b + 1, h:h + 1]), x.scale, causal=True, rows=rows)
         compare(ocpu[b:b + 1, h:h + 1, rows], lcpu[b:b + 1, h:h + 1, rows], ro, rl, "bf16", f"b={b} h={h}")
+
+
+@pytest.mark.parametrize("dtype,D,causal", [("f16", 64, True), ("bf16", 64, False), ("bf16", 128, True),
+                                             ("f16", 128, False), ("bf16", 96, True), ("f16", 32, True),
+                                             ("bf16", 256, True)])
+def test_forward_longest_first_order(dtype, D, causal):
+    """Key padding with whole heads on every XCD (B*H = 64, 8 per XCD): the workgroups of each XCD
+    find their units on the device in the order of decreasing key tiles. With kv_len = N
+    everywhere the result must be bit for bit that of the same launch without kv_len (another
+    order, the same arithmetic per unit; the outputs are prefilled with NaN, so a unit that
+    never ran shows up). With kv_len of 0, 1, 15, 64, 129, 333, N - 1 and N, every row against
+    the oracle."""
+    B, H, N = 8, 8, 700
+    x = generate(B, H, N, D, dtype, causal=causal, seed=5700 + D + int(causal))
+    say(f"longest-first order {dtype} D={D} causal={causal}")
+    o, lse = run_gpu(x)
+    o2, l2 = run_gpu(x, kv_len=np.full(B, N, dtype=np.int32))
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "longest-first order differs from the unpadded order"
+    kv = np.array([0, 1, 15, N - 1, N, 333, 64, 129], dtype=np.int32)
+    o3, l3 = run_gpu(x, kv_len=kv)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=causal, kv_len=kv)
+    compare(o3, l3, ro, rl, dtype, f"longest first D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("B", [64, 65])
+def test_forward_longest_first_limit(B):
+    """64 heads per XCD (B*H = 512) is the most the longest-first order takes, one per lane of a
+    wave; 65 (B*H = 520) goes head by head. Both with random kv_len, every row against the oracle."""
+    H, N, D = 8, 130, 64
+    x = generate(B, H, N, D, "bf16", causal=True, seed=5800 + B, padding=True)
+    say(f"longest-first limit B={B}")
+    o, lse = run_gpu(x)
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True, kv_len=x.kv_len)
+    compare(o, lse, ro, rl, "bf16", f"longest-first limit B={B}")
 
 
 def test_backward_rank_groups():
