@@ -502,15 +502,23 @@ int launch_bwd(const fa::BwdParams& base, int64_t B, int64_t H, int64_t N, hipSt
   p.n_tiles = (int)tiles;
   p.n_units = units;
   void* args[] = {&p};
-  const void* dq_fn = reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>);
+  // Key padding: both kernels take their units longest first (as the forward does).
+  const bool lpt = p.kv_len && !p.q_len && (B * H) % kXcds == 0 && B * H / kXcds <= 64;
+  const void* dq_fn = lpt ? reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves, true>)
+                          : reinterpret_cast<const void*>(&fa::bwd_dq_kernel<T, D, kBwdKeyTile, kBwdWaves>);
   p.tm_group = p.causal ? rank_group(B * H, N, D, sizeof(T), tiles, slots_per_xcd(stream, dq_fn, 64 * kBwdWaves)) : 1;
   hipError_t e = hipLaunchKernel(dq_fn, dim3((unsigned)units), dim3(64 * kBwdWaves), args, 0, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
   // K/V in LDS, eight waves (two per key group) at D >= 96: two waves per SIMD there.
   constexpr int kv_threads = D >= 96 ? 64 * 8 : 64 * kBwdWaves;
   const void* kv_fn;
-  if constexpr (D >= 96) kv_fn = reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>);
-  else kv_fn = reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>);
+  if constexpr (D >= 96) {
+    kv_fn = lpt ? reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8, true>)
+                : reinterpret_cast<const void*>(&fa::bwd_dkdv_lds_kernel<T, D, fa::kStatRows, 8>);
+  } else {
+    kv_fn = lpt ? reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves, true>)
+                : reinterpret_cast<const void*>(&fa::bwd_dkdv_kernel<T, D, fa::kStatRows, kBwdWaves>);
+  }
   p.tm_group = p.causal ? rank_group(B * H, N, D, sizeof(T), tiles, slots_per_xcd(stream, kv_fn, kv_threads)) : 1;
   e = hipLaunchKernel(kv_fn, dim3((unsigned)units), dim3(kv_threads), args, 0, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -169,7 +169,8 @@ template <int D> constexpr int dq_waves_per_eu() { return D <= 32 ? 3 : 2; }
 
 // ------------------------------------------------------------------------------------------
 // dQ (and Delta, exponent offsets): one workgroup per (b, h, query tile of 32*NW rows).
-template <typename T, int D, int BC, int NW>
+// LPT: the key-padded launch, whose workgroups take their query tiles longest first.
+template <typename T, int D, int BC, int NW, bool LPT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D>(), dq_waves_per_eu<D>()))) void bwd_dq_kernel(BwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -188,9 +189,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
   const int g = lane >> 5;
   const int r = lane & 31;
 
-  int bh;
-  int qt = decode_tile(p, blockIdx.x, &bh);
-  if (p.causal) qt = p.n_tiles - 1 - qt;  // longest query tiles first
+  int bh, qt;
+  if constexpr (LPT) {
+    // A head whose kv_len exceeds (t-1)*BC has n_tiles - floor((t-1)*BC/BR) query tiles with at
+    // least t key tiles under the causal mask (those from that index on), and all without it.
+    const int per_head = p.n_tiles;
+    const bool causal = p.causal != 0;
+    auto at_least = [&](int t, int kvl) {
+      if (t <= 0) return per_head;
+      if (kvl <= (t - 1) * BC) return 0;
+      return causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
+    };
+    longest_first(blockIdx.x, (int)(p.n_units / p.n_tiles), (int)p.H, per_head, (int)((p.N + BC - 1) / BC),
+                  p.kv_len, (int)p.N, true, at_least, &bh, &qt);
+  } else {
+    qt = decode_tile(p, blockIdx.x, &bh);
+    if (p.causal) qt = p.n_tiles - 1 - qt;  // longest query tiles first
+  }
   const int n = (int)p.N;
   const int64_t b_ = bh / p.H, h_ = bh % p.H;
   const T* Qh = reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h;
@@ -400,12 +415,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
   }
 }
 
+// Key tile of workgroup `bid` for the dK/dV kernels (BKV keys per tile, query tiles of BQ rows).
+// Without LPT: decode_tile's order. With LPT (the key-padded launch): longest first. A key tile
+// below kv_len is seen by ceil(N/BQ) query tiles, less floor(first key/BQ) under the causal mask,
+// and one at or past kv_len by none; so a head has min(ceil(kvl/BKV), ceil((NQ-t+1)*BQ/BKV)) key
+// tiles with at least t query tiles under the mask (ceil(kvl/BKV) for t <= NQ without it), its
+// tiles with the most work being the first.
+template <int BKV, int BQ, bool LPT>
+__device__ __forceinline__ int decode_key_tile(const BwdParams& p, int bid, int* bh) {
+  if constexpr (LPT) {
+    const int per_head = p.n_tiles;
+    const int n = (int)p.N;
+    const int nq = (n + BQ - 1) / BQ;
+    const bool causal = p.causal != 0;
+    auto at_least = [&](int t, int kvl) {
+      if (t <= 0) return per_head;
+      const int live = (kvl + BKV - 1) / BKV;  // key tiles below kv_len
+      if (!causal) return t <= nq ? live : 0;
+      const int lim = nq - t + 1;
+      return lim <= 0 ? 0 : min(live, (lim * BQ + BKV - 1) / BKV);
+    };
+    int kt;
+    longest_first(bid, (int)(p.n_units / p.n_tiles), (int)p.H, per_head, nq, p.kv_len, n, false, at_least, bh, &kt);
+    return kt;
+  } else {
+    return decode_tile(p, bid, bh);  // causal: key tile 0 has the most work
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // dK, dV: one workgroup per (b, h, key tile of 32*NW keys); query tiles of BQ rows.
 // Two waves per SIMD where the registers allow it; at D = 128 the K, V fragments and the dK, dV
 // accumulators alone take 192 registers, so one.
 
-template <typename T, int D, int BQ, int NW>
+template <typename T, int D, int BQ, int NW, bool LPT = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D>(), dkdv_waves_per_eu<D>())))
 void bwd_dkdv_kernel(BwdParams p) {
@@ -430,7 +473,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int r = lane & 31;
 
   int bh;
-  const int kt = decode_tile(p, blockIdx.x, &bh);  // causal: key tile 0 has the most work
+  const int kt = decode_key_tile<BKV, BQ, LPT>(p, blockIdx.x, &bh);
   const int n = (int)p.N;
   const int64_t b_ = bh / p.H, h_ = bh % p.H;
   const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h);
@@ -647,7 +690,7 @@ void bwd_dkdv_kernel(BwdParams p) {
 // and V live in LDS (64 KB, loaded once) and are read as B operands at each use. Eight waves: a
 // pair of waves shares each 32-key group, and wave w takes the 32-query half w / 4 of every
 // 64-row query tile; at the end the pair's partial dK and dV are added through LDS.
-template <typename T, int D, int BQ, int NW>
+template <typename T, int D, int BQ, int NW, bool LPT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_lds_kernel(BwdParams p) {
   using M = Mma<T>;
@@ -679,7 +722,7 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
   const int qh = wave >> 2;  // query half of each tile
 
   int bh;
-  const int kt = decode_tile(p, blockIdx.x, &bh);
+  const int kt = decode_key_tile<BKV, BQ, LPT>(p, blockIdx.x, &bh);
   const int n = (int)p.N;
   const int64_t b_ = bh / p.H, h_ = bh % p.H;
   const unsigned char* Qh = reinterpret_cast<const unsigned char*>(reinterpret_cast<const T*>(p.q) + b_ * p.st_q.b + h_ * p.st_q.h);

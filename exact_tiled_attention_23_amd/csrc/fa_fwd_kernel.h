@@ -165,61 +165,52 @@ __device__ __forceinline__ Unit decode_unit(const FwdParams& p, int bid) {
   return u;
 }
 
-// Work unit of workgroup `bid` for a key-padded problem (kv_len given, no q_len, no split, whole
-// heads on every XCD, at most 64 of them: the host checks all of this and then launches the
-// kernel instantiation that calls this). The work of a unit is its
-// number of key tiles, which under key padding differs between batch elements, and each XCD runs
-// its units in the order of decreasing work (ties in head-slot order, then by query tile from the
-// last), so that its longest units start first and the short ones fill the end. The host cannot
-// sort the units (kv_len lives on the device), so every wave finds its workgroup's place in that
-// order itself:
+// Longest-first order of the units of a key-padded problem (kv_len given, no q_len, no split,
+// whole heads on every XCD and at most 64 of them: the host checks all of this and then launches
+// the kernel instantiation that calls this). The work of a unit is its number of key tiles (or,
+// for a dK/dV unit, of query tiles), which under key padding differs between batch elements, and
+// each XCD runs its units in the order of decreasing work (ties in head-slot order), so that its
+// longest units start first and the short ones fill the end. The host cannot sort the units
+// (kv_len lives on the device), so every wave finds its workgroup's place in that order itself:
 //  * The XCD holds head slots [x*hx, (x+1)*hx) (slots run over the batch fastest, as in
 //    head_of_slot); lane s holds the kv_len of slot x*hx + s.
-//  * A head whose kv_len exceeds (t-1)*BC has per_head - floor((t-1)*BC/BR) units with at least
-//    t key tiles under the causal mask (its query tiles from that index on), and all per_head
-//    units without it; other heads have none. So the XCD's count of units with at least t tiles
-//    is that per-head count times the number of such heads (one ballot).
-//  * A binary search over t finds the work ts of the i-th unit (the largest t whose count exceeds
-//    i); the units of work exactly ts, taken head by head (a prefix sum over the lanes), give the
-//    head and, counted from its longest, the query tile.
+//  * at_least(t, kvl) gives the number of a head's units with at least t units of work, in closed
+//    form (per_head at t = 0, non-increasing in t); a wave sum gives the XCD's count.
+//  * A binary search over t finds the work ts of the i-th unit (the largest t whose count
+//    exceeds i). The units of work exactly ts, taken head by head (a prefix sum over the lanes),
+//    give the head and the unit's place among them; within a head the units of more work sit at
+//    the high end of the unit index (more_work_last: query tiles under the causal mask) or at the
+//    low end (key tiles of the dK/dV kernels), and the unit is counted from there.
 // All of it is wave-uniform: every wave of the workgroup finds the same unit.
-template <int BR, int BC>
-__device__ __forceinline__ Unit decode_unit_lpt(const FwdParams& p, int bid) {
-  const int heads = (int)p.BH, H = (int)p.H, B = heads / H, hx = heads / 8;
-  const int per_head = p.n_qtiles;
-  const int n = (int)p.N;
-  const bool causal = p.causal != 0;
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+template <class AtLeast>
+__device__ __forceinline__ void longest_first(int bid, int heads, int H, int per_head, int max_work,
+                                              const int32_t* kv_len, int n, bool more_work_last,
+                                              AtLeast at_least, int* bh, int* unit) {
+  const int B = heads / H, hx = heads / 8;
   const int x = bid % 8, i = bid / 8;
   const int lane = threadIdx.x & 63;
   int kv = -1;  // kv_len of this lane's head slot (lanes past hx hold none)
   if (lane < hx) {
-    const int v = p.kv_len[(x * hx + lane) % B];
+    const int v = kv_len[(x * hx + lane) % B];
     kv = v < 0 ? 0 : (v > n ? n : v);
   }
-  // Units of a head (kv_len kvl) with at least t key tiles.
-  auto at_least = [&](int t, int kvl) {
-    if (kvl < 0) return 0;
-    if (t <= 0) return per_head;
-    if (kvl <= (t - 1) * BC) return 0;
-    return causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
-  };
-  // The same over the XCD's heads.
-  auto count_at_least = [&](int t) {
-    if (t <= 0) return hx * per_head;
-    const int per = causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
-    return per * (int)__popcll(__ballot(kv > (t - 1) * BC));
-  };
-  int lo = 0, hi = (n + BC - 1) / BC + 1;  // count_at_least(lo) > i >= count_at_least(hi)
+  auto mine = [&](int t) { return kv < 0 ? 0 : at_least(t, kv); };
+  int lo = 0, hi = max_work + 1;  // count(lo) > i >= count(hi) = 0
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (count_at_least(mid) > i) lo = mid;
+    if (wave_sum(mine(mid)) > i) lo = mid;
     else hi = mid;
   }
   const int ts = lo;
-  const int j = i - count_at_least(ts + 1);  // place among the units of work exactly ts
-  const int above = at_least(ts + 1, kv);
-  const int e = at_least(ts, kv) - above;    // this head's units of work exactly ts
-  int pre = e;                                // inclusive prefix sum over the lanes
+  const int above = mine(ts + 1);
+  const int j = i - wave_sum(above);  // place among the XCD's units of work exactly ts
+  const int e = mine(ts) - above;     // this head's units of work exactly ts
+  int pre = e;                        // inclusive prefix sum over the lanes
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(pre, d);
@@ -230,13 +221,30 @@ __device__ __forceinline__ Unit decode_unit_lpt(const FwdParams& p, int bid) {
   sl = min(sl, hx - 1);
   const int jj = j - (__shfl(pre, sl) - __shfl(e, sl));
   const int above_s = __shfl(above, sl);
-  // The head's units of work ts are the query tiles just below those with more work.
-  int qt = (above_s > 0 ? per_head - above_s - 1 : per_head - 1) - jj;
-  qt = max(0, min(qt, per_head - 1));
+  int u = more_work_last ? per_head - 1 - above_s - jj : above_s + jj;
+  u = max(0, min(u, per_head - 1));
   const int slot = x * hx + sl;
+  // Wave-uniform values that came through lane moves: say so, so that the addresses formed from
+  // them stay in scalar registers.
+  *bh = __builtin_amdgcn_readfirstlane((slot % B) * H + slot / B);
+  *unit = __builtin_amdgcn_readfirstlane(u);
+}
+
+// Forward units (query tiles of BR rows, key tiles of BC) in the longest-first order. A head whose
+// kv_len exceeds (t-1)*BC has per_head - floor((t-1)*BC/BR) units with at least t key tiles under
+// the causal mask (its query tiles from that index on), and all of them without it.
+template <int BR, int BC>
+__device__ __forceinline__ Unit decode_unit_lpt(const FwdParams& p, int bid) {
+  const int per_head = p.n_qtiles;
+  const bool causal = p.causal != 0;
+  auto at_least = [&](int t, int kvl) {
+    if (t <= 0) return per_head;
+    if (kvl <= (t - 1) * BC) return 0;
+    return causal ? max(0, per_head - ((t - 1) * BC) / BR) : per_head;
+  };
   Unit u;
-  u.bh = (slot % B) * H + slot / B;
-  u.qt = qt;
+  longest_first(bid, (int)p.BH, (int)p.H, per_head, (int)((p.N + BC - 1) / BC), p.kv_len, (int)p.N, true,
+                at_least, &u.bh, &u.qt);
   u.split = 0;
   return u;
 }
