@@ -127,6 +127,20 @@ def test_forward_longest_first_limit(B):
     compare(o, lse, ro, rl, "bf16", f"longest-first limit B={B}")
 
 
+@pytest.mark.parametrize("dtype,D,causal", [("f16", 64, True), ("bf16", 64, False), ("bf16", 128, True),
+                                             ("f16", 96, True), ("bf16", 32, True)])
+def test_backward_longest_first_order(dtype, D, causal):
+    """Key padding with whole heads on every XCD (B*H = 64): the dQ and dK/dV kernels take their
+    units longest first, found on the device (key tiles past kv_len, with no work, come last).
+    kv_len of 0, 1, 15, 64, 129, 200, N - 1 and N, every gradient element against the oracle."""
+    B, H, N = 8, 8, 300
+    x = generate(B, H, N, D, dtype, causal=causal, seed=5900 + D + int(causal))
+    do = generate_grad_output(B, H, N, D, dtype, seed=5901 + D)
+    kv = np.array([0, 1, 15, N - 1, N, 200, 64, 129], dtype=np.int32)
+    say(f"longest-first backward {dtype} D={D} causal={causal}")
+    check(x, do, kv_len=kv, tag=f"longest first D={D} causal={causal}")
+
+
 def test_backward_rank_groups():
     """The backward kernels' units in groups of 8 heads (B*H = 72, N = 2048, D = 64, 16 units
     per head): bit for bit the result of the head-by-head order (kv_len = N)."""
