@@ -76,7 +76,8 @@ def test_split_rank_order():
 def test_forward_rank_groups():
     """B*H = 72 heads (9 per XCD), N = 2048, D = 64: rank by rank in groups of 8 heads (two
     [N, D] bf16 operands of 8 heads fill the 4 MB L2) plus a group of one. The same problem with
-    kv_len = N everywhere runs head by head; every unit's arithmetic is the same, so the two
+    kv_len = N everywhere takes the key-padded order (longest first, found on the device); every
+    unit's arithmetic is the same, so the two
     outputs must agree bit for bit (a unit that ran twice or never shows up, the outputs being
     prefilled with NaN). Sampled rows of three heads against the oracle."""
     B, H, N = 9, 8, 2048
@@ -143,7 +144,7 @@ def test_backward_longest_first_order(dtype, D, causal):
 
 def test_backward_rank_groups():
     """The backward kernels' units in groups of 8 heads (B*H = 72, N = 2048, D = 64, 16 units
-    per head): bit for bit the result of the head-by-head order (kv_len = N)."""
+    per head): bit for bit the result of the key-padded, longest-first order (kv_len = N)."""
     B, H, N, D = 9, 8, 2048, 64
     x = generate(B, H, N, D, "bf16", causal=True, seed=5600)
     do = generate_grad_output(B, H, N, D, "bf16", seed=5601)
