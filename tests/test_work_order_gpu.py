@@ -142,6 +142,36 @@ def test_backward_longest_first_order(dtype, D, causal):
     check(x, do, kv_len=kv, tag=f"longest first D={D} causal={causal}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_longest_first_strided_layouts(D):
+    """The key-padded longest-first order on [B, N, H, D] storage (token stride H*D), forward
+    and backward (B*H = 16, two heads per XCD): bit for bit the contiguous call, which the
+    oracle checks."""
+    B, H, N = 2, 8, 333
+    x = generate(B, H, N, D, "bf16", causal=True, seed=6100 + D)
+    do = generate_grad_output(B, H, N, D, "bf16", seed=6101 + D)
+    kv = torch.tensor([N - 40, 129], dtype=torch.int32)
+    dev = torch.device("cuda:0")
+    q, k, v, dO = (t.to(dev) for t in (x.q, x.k, x.v, do))
+    say(f"longest-first strided D={D}")
+    o, lse = fa.forward(q, k, v, causal=True, scale=x.scale, kv_len=kv)
+    grads = fa.backward(q, k, v, o, lse, dO, causal=True, scale=x.scale, kv_len=kv)
+    bnhd = lambda t: t.transpose(1, 2).contiguous().transpose(1, 2)
+    qs, ks, vs, dos = (bnhd(t) for t in (q, k, v, dO))
+    out = torch.full((B, N, H, D), float("nan"), dtype=q.dtype, device=dev).transpose(1, 2)
+    o2, l2 = fa.forward(qs, ks, vs, causal=True, scale=x.scale, kv_len=kv, out=out)
+    packed = torch.full((B, N, 3, H, D), float("nan"), dtype=q.dtype, device=dev)
+    dq, dk, dv = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    fa.backward(qs, ks, vs, bnhd(o), lse, dos, causal=True, scale=x.scale, kv_len=kv, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "strided forward differs from the contiguous call"
+    for a, b_, name in zip((dq, dk, dv), grads, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b_), f"strided {name} differs from the contiguous call"
+    ro, rl = oracle.attention(to_f64(x.q), to_f64(x.k), to_f64(x.v), x.scale, causal=True, kv_len=kv.numpy())
+    compare(o, lse, ro, rl, "bf16", f"longest first strided D={D}")
+    check(x, do, kv_len=kv.numpy(), tag=f"longest first strided D={D}")
+
+
 def test_backward_rank_groups():
     """The backward kernels' units in groups of 8 heads (B*H = 72, N = 2048, D = 64, 16 units
     per head): bit for bit the result of the key-padded, longest-first order (kv_len = N)."""
