@@ -4,7 +4,8 @@ Thirty configurations drawn once from a fixed seed cover combinations that the h
 cases do not name: B, H, ragged N up to 700, every head dimension, both 16-bit types (and
 float32 for the forward), causal or not, key padding with random kv_len (0 included), and a
 random part count for the split. Twenty more, from a second seed, add query padding (random
-q_len, with NaN in the padding rows of Q and dO), and forty more come from a third seed.
+q_len, with NaN in the padding rows of Q and dO), forty more come from a third seed, and sixteen
+more have key padding with B*H a multiple of 8, the launches whose units run longest first.
 Tolerances are the ones of the dedicated tests.
 """
 
@@ -42,8 +43,27 @@ def draw_configs(count=30, seed=2024, query_padding=False):
     return out
 
 
+def draw_whole_head_padded(count=16, seed=4242):
+    """Key padding with B*H a multiple of 8 (at most 64 heads per XCD): the launches that take
+    their units longest first, in an order each workgroup finds on the device."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        while True:
+            B, H = int(rng.choice([1, 2, 4, 8, 16])), int(rng.choice([1, 2, 4, 8]))
+            if (B * H) % 8 == 0 and B * H <= 64:
+                break
+        dtype = ["bf16", "f16"][int(rng.integers(0, 2))]
+        D = int(rng.choice([32, 64, 96, 128, 256]))
+        N = int(rng.integers(1, 401))
+        kv = rng.integers(0, N + 1, size=B).astype(np.int32)
+        out.append((i, B, H, N, D, dtype, bool(rng.integers(0, 2)), kv, int(rng.integers(2, 9)), None))
+    return out
+
+
 CONFIGS = (draw_configs() + [(100 + c[0],) + c[1:] for c in draw_configs(20, seed=77, query_padding=True)]
-           + [(200 + c[0],) + c[1:] for c in draw_configs(40, seed=31337)])
+           + [(200 + c[0],) + c[1:] for c in draw_configs(40, seed=31337)]
+           + [(300 + c[0],) + c[1:] for c in draw_whole_head_padded()])
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"c{c[0]}")
