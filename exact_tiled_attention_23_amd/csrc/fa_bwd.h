@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
-  const float c = p.scale_log2;
+  const float c = in_vgpr(p.scale_log2);  // the scaling FMAs read vector registers only (+1-2% at D <= 96)
 
   auto issue = [&](int t, int buf) {
     const unsigned kl = lds_address(lds + buf * 2 * TILEB);
@@ -529,7 +529,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     dka[t] = f32x16{};
     dva[t] = f32x16{};
   }
-  const float c = p.scale_log2;
+  const float c = in_vgpr(p.scale_log2);  // the scaling FMAs read vector registers only (+1-2% at D <= 96)
   // Stats copy: lanes 0-31 bring the 512-byte block of 64 offsets and 64 values of -Delta,
   // lanes 32-63 the same bytes again (the copy instruction always moves 1 KB).
   const unsigned stat_off = (unsigned)(lane & 31) * 16;
@@ -786,7 +786,7 @@ void bwd_dkdv_lds_kernel(BwdParams p) {
     dka[t] = f32x16{};
     dva[t] = f32x16{};
   }
-  const float c = p.scale_log2;
+  const float c = in_vgpr(p.scale_log2);  // the scaling FMAs read vector registers only (+1-2% at D <= 96)
 
   for (int t = t0; t < nqt; ++t) {
     const int i0 = t * BQ;

@@ -34,6 +34,16 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// A wave-uniform value moved into a vector register once. A VOP3 instruction that reads a
+// scalar register (v_fma_f32 with the softmax scale, a kernel argument) issues about one cycle
+// slower per SIMD than the same instruction on vector registers alone once two or more waves
+// share the SIMD: measured on gfx950 with register-only loops, 3.56 against 2.56 cycles per
+// v_fma_f32 at two waves per SIMD and 3.03 against 2.04 at three.
+__device__ __forceinline__ float in_vgpr(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Per-element-type matrix-core step. KPER: reduction elements a lane holds per
 // operand per instruction; one instruction reduces over KSTEP = 2*KPER elements
 // (lanes 0-31 hold the first KPER, lanes 32-63 the next KPER).
