@@ -112,6 +112,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
   const float c = p.scale_log2;
   const int krow_a = a_row_key<KPER>(r);
 
+  // A tile's rows at or past kv_hi are loaded from row kv_hi - 1 (in bounds: a tile is loaded
+  // only when the block has a key) and stored to LDS as zeros. The loads themselves take no
+  // branch: a load under a per-row branch made the compiler wait for it inside the branch, one
+  // memory round trip for every second row of the first tile.
   uint4 kreg[K_UNITS];
   uint4 vreg[V_UNITS][V_ROWS];
   auto load_tile = [&](int64_t j0) {
@@ -120,8 +124,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
       const int cidx = lane + n * 64;
       const int row = cidx / CPR;
       const int col = (cidx % CPR) * CH;
-      const int64_t key = j0 + row;
-      kreg[n] = key < kv_hi ? *reinterpret_cast<const uint4*>(Kh + key * ksn + col) : uint4{0, 0, 0, 0};
+      const int64_t key = j0 + row < kv_hi ? j0 + row : kv_hi - 1;
+      kreg[n] = *reinterpret_cast<const uint4*>(Kh + key * ksn + col);
     }
 #pragma unroll
     for (int n = 0; n < V_UNITS; ++n) {
@@ -130,22 +134,29 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
       const int col = (cidx % CPR) * CH;
 #pragma unroll
       for (int e = 0; e < V_ROWS; ++e) {
-        const int64_t key = j0 + row0 + e;
-        vreg[n][e] = key < kv_hi ? *reinterpret_cast<const uint4*>(Vh + key * vsn + col) : uint4{0, 0, 0, 0};
+        const int64_t key = j0 + row0 + e < kv_hi ? j0 + row0 + e : kv_hi - 1;
+        vreg[n][e] = *reinterpret_cast<const uint4*>(Vh + key * vsn + col);
       }
     }
   };
-  auto store_tile = [&]() {
+  // Zero the words of a row at or past kv_hi (component selects: a select of the vector type
+  // as a whole went through scratch memory).
+  auto live4 = [](uint4 x, bool live) __attribute__((always_inline)) {
+    return uint4{live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u};
+  };
+  auto store_tile = [&](int64_t j0) {
 #pragma unroll
     for (int n = 0; n < K_UNITS; ++n) {
       const int cidx = lane + n * 64;
-      *reinterpret_cast<uint4*>(&k_lds[(cidx / CPR) * KLD + (cidx % CPR) * CH]) = kreg[n];
+      *reinterpret_cast<uint4*>(&k_lds[(cidx / CPR) * KLD + (cidx % CPR) * CH]) = live4(kreg[n], j0 + cidx / CPR < kv_hi);
     }
 #pragma unroll
     for (int n = 0; n < V_UNITS; ++n) {
       const int cidx = lane + n * 64;
       const int row0 = (cidx / CPR) * V_ROWS;
       const int col = (cidx % CPR) * CH;
+#pragma unroll
+      for (int e = 0; e < V_ROWS; ++e) vreg[n][e] = live4(vreg[n][e], j0 + row0 + e < kv_hi);
       if constexpr (sizeof(T) == 2) {
         // Two consecutive keys per 32-bit word of V^T.
         const uint32_t a[4] = {vreg[n][0].x, vreg[n][0].y, vreg[n][0].z, vreg[n][0].w};
@@ -164,13 +175,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
     }
   };
 
+  int t = wave;
+  if (t < n_tiles) load_tile((int64_t)t * BC);  // in flight with the Q rows, and while the fragments are read
 #pragma unroll
   for (int n = 0; n < K_UNITS; ++n) {
     const int cidx = lane + n * 64;
     *reinterpret_cast<uint4*>(&k_lds[(cidx / CPR) * KLD + (cidx % CPR) * CH]) = qreg[n];
   }
-  int t = wave;
-  if (t < n_tiles) load_tile((int64_t)t * BC);  // in flight while the fragments are read
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -183,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
     // the fences keep the compiler from moving this tile's stores above the previous tile's
     // reads, or this tile's reads above its stores.
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    store_tile();
+    store_tile(j0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -192,9 +203,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
     // ---- S^T = K . Q^T for the tile's 32 keys
     f32x16 s = f32x16{};
     {
+      // The K fragments are read PF steps ahead of their products, so an LDS read's latency
+      // passes under earlier products instead of stalling the chain at every step.
+      constexpr int PF = NQF < 8 ? NQF : 8;
       const T* arow = &k_lds[krow_a * KLD + KPER * g];
+      frag kf[NQF];
 #pragma unroll
-      for (int st = 0; st < NQF; ++st) s = M::run(*reinterpret_cast<const frag*>(arow + KSTEP * st), qf[st], s);
+      for (int st = 0; st < PF; ++st) kf[st] = *reinterpret_cast<const frag*>(arow + KSTEP * st);
+#pragma unroll
+      for (int st = 0; st < NQF; ++st) {
+        if (st + PF < NQF) kf[st + PF] = *reinterpret_cast<const frag*>(arow + KSTEP * (st + PF));
+        s = M::run(kf[st], qf[st], s);
+      }
+      // Pin that order (left alone, the scheduler moves each read back next to its product).
+      // Two consecutive float fragments merge into one ds_read2_b32.
+      constexpr int RD = KPER == 1 ? 2 : 1;  // fragments per LDS read instruction
+      __builtin_amdgcn_sched_group_barrier(0x100, PF / RD, 0);
+#pragma unroll
+      for (int st = 0; st < NQF; st += RD) {
+        __builtin_amdgcn_sched_group_barrier(0x008, RD, 0);
+        if (st + PF < NQF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     // ---- masks (edge tiles; rows at or past N are never stored and need none)
     const bool need_mask = (j0 + BC > kvl) || (p.causal && j0 + BC - 1 > q0) || (nq < N && q0 + 32 > nq);
