@@ -242,21 +242,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(dq_wave
   const int ntiles = kv_hi > 0 ? (kv_hi + BC - 1) / BC : 0;
 
   // ---- Q^T and dO^T fragments (B operands), Delta = rowsum(dO o O), exponent offset. A
-  // padding row is not read: zero fragments, Delta 0 and an empty row's offset make its P, dS
-  // and dQ exactly 0.
+  // padding row gets zero fragments, Delta 0 and an empty row's offset, which make its P, dS
+  // and dQ exactly 0. At D <= 96 its loads read row min(qrow, n - 1) (in bounds) and are
+  // discarded by selects, so no load sits under a branch: under a per-row branch the compiler
+  // waited for each step's loads before issuing the next step's (a memory round trip per 16
+  // columns). At D = 128 all of them in flight at once take registers that are not free (the
+  // kernel then spilled inside its key loop), and the padding row is not read instead.
   frag qf[NQF], dof[NQF];
   float dsum = 0.f;
+  if constexpr (D <= 96) {
+    const bool qlive = qrow < nq;
+    const int64_t qrow_ld = qrow < n ? qrow : n - 1;
 #pragma unroll
-  for (int s = 0; s < NQF; ++s) {
-    if (qrow < nq) {
-      qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * p.st_q.n + 16 * s + 8 * g);
-      dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * p.st_do.n + 16 * s + 8 * g);
-      const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * p.st_o.n + 16 * s + 8 * g);
+    for (int s = 0; s < NQF; ++s) {
+      qf[s] = *reinterpret_cast<const frag*>(Qh + qrow_ld * p.st_q.n + 16 * s + 8 * g);
+      dof[s] = *reinterpret_cast<const frag*>(dOh + qrow_ld * p.st_do.n + 16 * s + 8 * g);
+    }
+#pragma unroll
+    for (int s = 0; s < NQF; ++s) {
+      const frag of = *reinterpret_cast<const frag*>(Oh + qrow_ld * p.st_o.n + 16 * s + 8 * g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)dof[s][e], (float)of[e], dsum);
-    } else {
-      qf[s] = frag{};
-      dof[s] = frag{};
+    }
+    dsum = qlive ? dsum : 0.f;
+#pragma unroll
+    for (int s = 0; s < NQF; ++s) {
+      qf[s] = qlive ? qf[s] : frag{};
+      dof[s] = qlive ? dof[s] : frag{};
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NQF; ++s) {
+      if (qrow < nq) {
+        qf[s] = *reinterpret_cast<const frag*>(Qh + (int64_t)qrow * p.st_q.n + 16 * s + 8 * g);
+        dof[s] = *reinterpret_cast<const frag*>(dOh + (int64_t)qrow * p.st_do.n + 16 * s + 8 * g);
+        const frag of = *reinterpret_cast<const frag*>(Oh + (int64_t)qrow * p.st_o.n + 16 * s + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)dof[s][e], (float)of[e], dsum);
+      } else {
+        qf[s] = frag{};
+        dof[s] = frag{};
+      }
     }
   }
   const float delta = pair_sum(dsum);

@@ -283,10 +283,6 @@ void fwd16_kernel(FwdParams p) {
     if (qrow < nq) qf[s] = *reinterpret_cast<const frag*>(Qh + qrow * qsn + 16 * s + 8 * g);
     else qf[s] = frag{};  // padding rows are not read (they may hold anything)
   }
-  // Consume the Q fragments here, so the compiler's wait for them is placed before the
-  // loop rather than re-issued (as a full vmcnt wait) in every iteration.
-#pragma unroll
-  for (int s = 0; s < NQF; ++s) asm volatile("" ::"v"(qf[s]));
 
   // ---- per-lane LDS read offsets
   const int kr = a_row_key<8>(r);                 // K row this lane feeds as A-operand row r
@@ -526,6 +522,11 @@ void fwd16_kernel(FwdParams p) {
   };
   auto tile_loop = [&]() __attribute__((always_inline)) {
     if (t_lo < t_hi) issue_tile(t_lo * BC, Int<0>{});
+    // Consume the Q fragments here: the compiler's wait for them is then placed before the loop
+    // rather than re-issued (as a full vmcnt wait) in every iteration, and it comes after the
+    // first tile's copies are issued, so the two loads' latencies overlap.
+#pragma unroll
+    for (int s = 0; s < NQF; ++s) asm volatile("" ::"v"(qf[s]));
     for (int i = 0; i < steps; i += 2) {
       tile_step(t_lo + i, Int<0>{});
       if (i + 1 >= steps) break;
