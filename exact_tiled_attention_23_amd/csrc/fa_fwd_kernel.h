@@ -4,8 +4,8 @@
 // Core algorithm: for each batch, head and query block, loop over key/value blocks).
 // NW waves of 64 lanes each own 32 consecutive query rows. Per key/value tile:
 //
-//   stage   K tile -> LDS row-major, V tile -> LDS transposed (V^T), from 16-byte
-//           coalesced global loads that were issued one tile ahead into registers;
+//   stage   K tile -> LDS row-major, V tile -> LDS transposed (V^T; row-major for float32),
+//           from 16-byte coalesced global loads that were issued one tile ahead into registers;
 //   S^T     = K . Q^T on 32x32 MFMA (fp32 accumulate). With this orientation the
 //           accumulator layout puts one query per lane (lane % 32) and half of the
 //           tile's keys in each 32-lane half, so row statistics stay in registers;
@@ -295,7 +295,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   static_assert((BC * CPR) % NT == 0, "K staging must divide evenly");
 
   __shared__ __attribute__((aligned(16))) T k_lds[BC * KLD];
-  __shared__ __attribute__((aligned(16))) T vt_lds[D * VLD];
+  // V^T for 16-bit types; for float32, V row-major (stride KLD, like K): a float32 A-operand
+  // fragment of the P.V product is one element per lane, V[key][d] with d along the lanes, which
+  // a row-major tile serves directly, and 16-byte writes replace a transposed copy's
+  // bank-conflicted single-word writes.
+  constexpr int VELEMS = sizeof(T) == 4 && BC * KLD > D * VLD ? BC * KLD : D * VLD;
+  __shared__ __attribute__((aligned(16))) T vt_lds[VELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -422,10 +427,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
           *reinterpret_cast<uint32_t*>(&vt_lds[(col + 2 * w + 1) * VLD + row0]) = hi;
         }
       } else {
-        const float f[4] = {__uint_as_float(vreg[n][0].x), __uint_as_float(vreg[n][0].y),
-                            __uint_as_float(vreg[n][0].z), __uint_as_float(vreg[n][0].w)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vt_lds[(col + e) * VLD + row0] = f[e];
+        *reinterpret_cast<uint4*>(&vt_lds[row0 * KLD + col]) = vreg[n][0];
       }
     }
   };
@@ -506,7 +508,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const frag a = *reinterpret_cast<const frag*>(&vt_lds[(32 * dt + r) * VLD + KSTEP * kk + KPER * g]);
+          const frag a = sizeof(T) == 4 ? *reinterpret_cast<const frag*>(&vt_lds[(KSTEP * kk + g) * KLD + 32 * dt + r])
+                                        : *reinterpret_cast<const frag*>(&vt_lds[(32 * dt + r) * VLD + KSTEP * kk + KPER * g]);
           oacc[dt] = M::run(a, pf, oacc[dt]);
         }
       }

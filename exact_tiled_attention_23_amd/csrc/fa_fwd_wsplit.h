@@ -14,7 +14,7 @@
 //     O = (sum_w a_w O_w) / l,   LSE = (m + log2 l) ln 2,
 //
 // through LDS inside the workgroup, so the call needs no workspace. A wave's tile is 32 keys,
-// staged global -> registers -> the wave's own LDS region (K row-major, V transposed), with the
+// staged global -> registers -> the wave's own LDS region (K and V row-major), with the
 // next tile's loads in flight while the current one is computed; the waves touch only their own
 // LDS until the merge, so they need no barrier before it. The arithmetic per tile is that of
 // fwd_kernel in fa_fwd_kernel.h (S^T = K . Q^T, masks, base-2 online softmax, O^T += V^T . P^T).
@@ -37,10 +37,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
   constexpr int CH = 16 / (int)sizeof(T);         // elements per 16-byte chunk
   constexpr int CPR = D / CH;                     // chunks per row
   constexpr int KLD = D + CH;                     // K row stride in LDS (padded by 16 bytes)
-  constexpr int VLD = BC + CH;                    // V^T row stride in LDS
+  constexpr int VLD = BC + CH;                    // V^T row stride in LDS (16-bit types)
   constexpr int NDT = D / 32;
   constexpr int NQF = D / KSTEP;
-  constexpr int WAVE_ELEMS = BC * KLD + D * VLD;  // one wave's K and V^T tiles
+  constexpr int WAVE_ELEMS = BC * KLD + D * VLD;  // one wave's K and V tiles (V row-major for float32)
+  static_assert(BC * KLD <= D * VLD, "a row-major V tile fits in the V area");
   constexpr int K_UNITS = BC * CPR / 64;          // 16-byte K chunks per lane per tile
   constexpr int V_ROWS = (sizeof(T) == 2) ? 2 : 1;
   constexpr int V_UNITS = (BC / V_ROWS) * CPR / 64;
@@ -167,10 +168,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
           *reinterpret_cast<uint32_t*>(&vt_lds[(col + 2 * w + 1) * VLD + row0]) = (a[w] >> 16) | (bb[w] & 0xffff0000u);
         }
       } else {
-        const float f[4] = {__uint_as_float(vreg[n][0].x), __uint_as_float(vreg[n][0].y),
-                            __uint_as_float(vreg[n][0].z), __uint_as_float(vreg[n][0].w)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vt_lds[(col + e) * VLD + row0] = f[e];
+        // float32: V stays row-major (one 16-byte write per chunk, like K). A float32 A-operand
+        // fragment of the P.V product is one element per lane, V[key][d] with d along the lanes,
+        // which a row-major tile serves directly; a transposed copy took 32 single-word writes
+        // per lane and tile, with bank conflicts, and its LDS traffic held up the other waves.
+        *reinterpret_cast<uint4*>(&vt_lds[row0 * KLD + col]) = vreg[n][0];
       }
     }
   };
@@ -264,7 +266,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_wsplit_kernel(FwdParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const frag a = *reinterpret_cast<const frag*>(&vt_lds[(32 * dt + r) * VLD + KSTEP * kk + KPER * g]);
+        const frag a = sizeof(T) == 4 ? *reinterpret_cast<const frag*>(&vt_lds[(KSTEP * kk + g) * KLD + 32 * dt + r])
+                                      : *reinterpret_cast<const frag*>(&vt_lds[(32 * dt + r) * VLD + KSTEP * kk + KPER * g]);
         oacc[dt] = M::run(a, pf, oacc[dt]);
       }
     }
